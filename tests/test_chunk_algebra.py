@@ -1,0 +1,99 @@
+"""The chunked (WY / UT) form used by the GPU kernels, in plain fp64, equals the
+token recurrence of the oracle.
+
+This checks the algebra only (no kernel, no rounding): a chunk of L <= 64
+tokens, split into 16-token sub-chunks with per-sub-chunk reference points so
+that every factorised exponential stays inside fp32 range when
+lower_bound >= -5 (|sum of 16 gates| <= 80 < ln(FLT_MAX)).
+
+Within a chunk with start state S0 (V x K), cumulative gates G_r (per channel)
+and Gamma_r = exp(G_r):
+    A   = StrictLower(diag(beta) (K^.Gamma)(K^/Gamma)^T)
+    Tm  = (I + A)^-1
+    W   = Tm diag(beta) (K^.Gamma),   U~ = Tm diag(beta) V
+    U   = U~ - W S0^T
+    O   = scale [(Q^.Gamma) S0^T + Lower((Q^.Gamma)(K^/Gamma)^T) U]
+    S1  = S0 Diag(Gamma_L) + U^T (K^.Gamma_L/Gamma)
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import kda_oracle
+import kda_inputs
+
+
+def chunk_forward(q, k, v, g, b, A_log, dt, lb, scale, S0, C=64, SUB=16):
+    """fp64 chunked form for one (sequence, head). q,k,g [T,K]; v [T,V]; b [T]."""
+    T, K = q.shape
+    S = S0.copy()
+    out = np.zeros((T, v.shape[1]))
+    rate = math.exp(A_log)
+    for c0 in range(0, T, C):
+        L = min(C, T - c0)
+        qq = q[c0:c0 + L] / np.sqrt((q[c0:c0 + L] ** 2).sum(1, keepdims=True) + 1e-6)
+        kk = k[c0:c0 + L] / np.sqrt((k[c0:c0 + L] ** 2).sum(1, keepdims=True) + 1e-6)
+        vv = v[c0:c0 + L]
+        beta = 1 / (1 + np.exp(-b[c0:c0 + L]))
+        gate = lb / (1 + np.exp(-rate * (g[c0:c0 + L] + dt)))
+        nsub = (L + SUB - 1) // SUB
+        # sub-chunk local cumulative gates and reference points
+        Gs = np.zeros((L, K))
+        ref = np.zeros((nsub + 1, K))
+        for w in range(nsub):
+            a, e = w * SUB, min(L, (w + 1) * SUB)
+            Gs[a:e] = np.cumsum(gate[a:e], axis=0)
+            ref[w + 1] = ref[w] + Gs[e - 1]
+        sub = np.arange(L) // SUB
+        G = Gs + ref[sub]                           # chunk-relative cumulative gate
+        A = np.zeros((L, L))
+        Aqk = np.zeros((L, L))
+        for wa in range(nsub):
+            ra = slice(wa * SUB, min(L, (wa + 1) * SUB))
+            erow = np.exp(Gs[ra])                   # <= 1
+            for wb in range(wa + 1):
+                rb = slice(wb * SUB, min(L, (wb + 1) * SUB))
+                if wb == wa:
+                    col = kk[rb] * np.exp(-Gs[rb])  # <= e^80 when lb >= -5
+                    A[ra, rb] = np.tril((kk[ra] * erow) @ col.T, -1)
+                    Aqk[ra, rb] = np.tril((qq[ra] * erow) @ col.T, 0)
+                else:
+                    end_b = ref[wb + 1]
+                    col = kk[rb] * np.exp(end_b - G[rb])          # <= 1
+                    d = np.exp(ref[wa] - end_b)                   # <= 1
+                    A[ra, rb] = (kk[ra] * erow * d) @ col.T
+                    Aqk[ra, rb] = (qq[ra] * erow * d) @ col.T
+        A = beta[:, None] * A
+        Tm = np.linalg.inv(np.eye(L) + A)
+        Gam = np.exp(G)
+        W = Tm @ (beta[:, None] * kk * Gam)
+        Ut = Tm @ (beta[:, None] * vv)
+        U = Ut - W @ S.T
+        out[c0:c0 + L] = scale * ((qq * Gam) @ S.T + Aqk @ U)
+        GL = ref[nsub]
+        S = S * np.exp(GL)[None, :] + U.T @ (kk * np.exp(GL[None, :] - G))
+    return out, S
+
+
+@pytest.mark.parametrize("T,lb", [(150, -5.0), (64, -2.0), (200, 0.0), (17, -5.0), (129, -0.3)])
+def test_chunk_form_equals_recurrence(T, lb):
+    d = kda_inputs.make_inputs(kda_inputs.custom(T=T, H=2, seed=31, state='fp32', lower_bound=lb))
+    S0 = d['initial_state'].double().numpy()
+    out, fin = kda_oracle(d['q'], d['k'], d['v'], d['g'], d['beta'], d['scale'], d['A_log'],
+                          d['dt_bias'], d['lower_bound'], initial_state=d['initial_state'])
+    f = lambda t: t.float().double().numpy()
+    for h in range(2):
+        o, S = chunk_forward(f(d['q'])[0, :, h], f(d['k'])[0, :, h], f(d['v'])[0, :, h],
+                             f(d['g'])[0, :, h], f(d['beta'])[0, :, h], float(d['A_log'][h]),
+                             f(d['dt_bias'])[h], float(np.float32(lb)), float(np.float32(d['scale'])),
+                             S0[0, h])
+        np.testing.assert_allclose(o, out[:, h], rtol=1e-9, atol=1e-12)
+        np.testing.assert_allclose(S, fin[0, h], rtol=1e-9, atol=1e-12)
+
+
+def test_factorised_exponentials_stay_in_fp32_range():
+    """With lb >= -5 every factor the kernels form is within fp32 range."""
+    lb, SUB = -5.0, 16
+    worst = -lb * SUB                               # |sum of 16 gates| < 80
+    assert worst < math.log(np.finfo(np.float32).max)
