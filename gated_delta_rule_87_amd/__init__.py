@@ -1,0 +1,173 @@
+"""MI355X (gfx950) Kimi Delta Attention forward -- Python binding of libkda.so.
+
+Argument marshalling only: every step of the forward runs in the HIP kernels
+behind the C ABI declared in include/kda.h. PyTorch provides device memory
+(including the workspace, from its caching allocator) and the current stream.
+
+    import gated_delta_rule_87_amd as kda
+    kda.fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+            initial_state=None, final_state=None, cu_seqlens=None)
+
+mirrors ``flash_kda.fwd`` and its parameter table ("Kernel API" of the
+FlashKDA README digest): q, k, g bf16 [B, T, H, 128]; v bf16 [B, T, H, 128];
+beta bf16 [B, T, H] (logits); out bf16 [B, T, H, 128] written in place;
+A_log fp32 [H]; dt_bias fp32 [H, 128]; lower_bound in [-5, 0]; states bf16 or
+fp32 [B|N, H, 128, 128] with equal dtypes; cu_seqlens int64 [N+1] with B = 1.
+Returns None. There is no CPU fallback: if libkda.so is missing or fails to
+load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["fwd", "fwd_recurrent", "workspace_size", "lib", "KDAError", "status_string", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+
+STATE_NONE, STATE_BF16, STATE_FP32 = 0, 1, 2
+_STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE", 4: "KDA_ERR_VALUE",
+           5: "KDA_ERR_ALIGN", 6: "KDA_ERR_WORKSPACE", 7: "KDA_ERR_HIP"}
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{msg} (status {code})")
+        self.code = code
+
+
+def lib():
+    """Load libkda.so (built in-tree by gated_delta_rule_87_amd.build). Raises if missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libkda.so not built ({LIB_PATH}); run python -m gated_delta_rule_87_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        F = ctypes.c_float
+        L.kda_fwd_workspace_size.restype = ctypes.c_size_t
+        L.kda_fwd_workspace_size.argtypes = [I64, I64, I64, I64]
+        L.kda_fwd.restype = I
+        L.kda_fwd.argtypes = [P, P, P, P, P, F, P, P, P, F, P, I, P, I, P, I64, I64, I64, I64, I64, I64, P,
+                              ctypes.c_size_t, P]
+        L.kda_fwd_recurrent.restype = I
+        L.kda_fwd_recurrent.argtypes = [P, P, P, P, P, F, P, P, P, F, P, I, P, I, P, I64, I64, I64, I64, I64,
+                                        I64, P]
+        L.kda_status_string.restype = ctypes.c_char_p
+        L.kda_status_string.argtypes = [I]
+        L.kda_version.restype = ctypes.c_char_p
+        L.kda_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().kda_status_string(int(code)).decode()
+
+
+def workspace_size(B: int, T: int, H: int, N: int = 0) -> int:
+    """Bytes of workspace kda_fwd needs (N = number of sequences with cu_seqlens, else 0)."""
+    return int(lib().kda_fwd_workspace_size(int(B), int(T), int(H), int(N)))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(name, t, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _state_code(t: Optional[torch.Tensor]) -> int:
+    if t is None:
+        return STATE_NONE
+    if t.dtype == torch.bfloat16:
+        return STATE_BF16
+    if t.dtype == torch.float32:
+        return STATE_FP32
+    raise ValueError(f"state must be bf16 or fp32, got {t.dtype}")
+
+
+def _prepare(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens):
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a 4-D tensor [B, T, H, K]")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    B, T, H, K = q.shape
+    V = v.shape[-1] if isinstance(v, torch.Tensor) and v.dim() == 4 else -1
+    if K != 128 or V != 128:
+        raise ValueError(f"K = V = 128 is required (got K={K}, V={V})")
+    for name, t in (("q", q), ("k", k), ("g", g)):
+        _check(name, t, torch.bfloat16, (B, T, H, K), dev)
+    _check("v", v, torch.bfloat16, (B, T, H, V), dev)
+    _check("beta", beta, torch.bfloat16, (B, T, H), dev)
+    _check("out", out, torch.bfloat16, (B, T, H, V), dev)
+    _check("A_log", A_log, torch.float32, (H,), dev)
+    _check("dt_bias", dt_bias, torch.float32, (H, K), dev)
+    N = 0
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError("cu_seqlens requires B == 1")
+        if cu_seqlens.dtype != torch.int64 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be int64 [N+1] with N >= 1")
+        _check("cu_seqlens", cu_seqlens, torch.int64, tuple(cu_seqlens.shape), dev)
+        N = cu_seqlens.numel() - 1
+    nseq = N if cu_seqlens is not None else B
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None:
+            _check(name, t, t.dtype, (nseq, H, V, K), dev)
+            _state_code(t)
+    if initial_state is not None and final_state is not None and initial_state.dtype != final_state.dtype:
+        raise ValueError("initial_state and final_state must have the same dtype")
+    return B, T, H, K, V, N
+
+
+def _stream_ptr(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def fwd(q, k, v, g, beta, scale: float, out, A_log, dt_bias, lower_bound: float,
+        initial_state=None, final_state=None, cu_seqlens=None, workspace: Optional[torch.Tensor] = None):
+    """Chunked KDA forward; writes ``out`` (and ``final_state``) in place, returns None."""
+    B, T, H, K, V, N = _prepare(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens)
+    L = lib()
+    ws_bytes = workspace_size(B, T, H, N)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < ws_bytes or workspace.device != q.device:
+        raise ValueError(f"workspace must hold {ws_bytes} bytes on {q.device}")
+    rc = L.kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(out), _ptr(A_log),
+                   _ptr(dt_bias), float(lower_bound), _ptr(initial_state), _state_code(initial_state),
+                   _ptr(final_state), _state_code(final_state), _ptr(cu_seqlens), N, B, T, H, K, V,
+                   _ptr(workspace), workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
+    if rc != 0:
+        raise KDAError(rc, status_string(rc))
+    return None
+
+
+def fwd_recurrent(q, k, v, g, beta, scale: float, out, A_log, dt_bias, lower_bound: float,
+                  initial_state=None, final_state=None, cu_seqlens=None):
+    """Token-by-token KDA forward (online generation / reference); same contract as fwd."""
+    B, T, H, K, V, N = _prepare(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens)
+    rc = lib().kda_fwd_recurrent(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(out),
+                                 _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state),
+                                 _state_code(initial_state), _ptr(final_state), _state_code(final_state),
+                                 _ptr(cu_seqlens), N, B, T, H, K, V, _stream_ptr(q.device))
+    if rc != 0:
+        raise KDAError(rc, status_string(rc))
+    return None

@@ -1,0 +1,221 @@
+// kda_api.cpp -- C ABI of libkda.so: argument validation, workspace layout and
+// the launch sequence of the chunked KDA forward on the caller's HIP stream.
+//
+// Argument list and rules follow flash_kda.fwd and its parameter table
+// ("Kernel API" of the FlashKDA README digest, aiwatch.icu page) and the
+// caller-owned in-place `out` of the 2kiu.com guide (sections 一 and 三):
+// K = V = 128; bf16 q/k/v/g/beta/out; fp32 A_log/dt_bias; lower_bound in
+// [-5, 0]; optional bf16/fp32 states of equal dtype; cu_seqlens requires B = 1.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#include "../../include/kda.h"
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+
+inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct Layout {
+  int64_t max_chunks = 0;
+  size_t rec = 0, seq_tab = 0, chunk_tab = 0, seq_start = 0, total = 0;
+};
+
+// Workspace regions: chunk records | seq_tab | chunk_tab | seq_start.
+bool make_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool varlen, Layout& L) {
+  if (B < 1 || T < 0 || H < 1 || N < 0) return false;
+  if (varlen) {
+    L.max_chunks = T / kda::CH + N;
+  } else {
+    L.max_chunks = B * ((T + kda::CH - 1) / kda::CH);
+  }
+  if (L.max_chunks > INT32_MAX / 2) return false;
+  const size_t rec = (size_t)L.max_chunks * (size_t)H * (size_t)kda::REC_BYTES;
+  size_t off = 0;
+  L.rec = off;
+  off = align_up(off + rec);
+  L.seq_tab = off;
+  off = align_up(off + (varlen ? (size_t)N * sizeof(int2) : 0));
+  L.chunk_tab = off;
+  off = align_up(off + (varlen ? (size_t)L.max_chunks * sizeof(int2) : 0));
+  L.seq_start = off;
+  off = align_up(off + (varlen ? (size_t)N * sizeof(int32_t) : 0));
+  L.total = off;
+  return true;
+}
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool env_flag(const char* name) {
+  const char* s = std::getenv(name);
+  return s && s[0] == '1';
+}
+
+// Shared argument checks of both entry points.
+int check_common(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,
+                 const void* out, const float* A_log, const float* dt_bias, float lower_bound,
+                 const void* initial_state, int initial_dtype, const void* final_state, int final_dtype,
+                 const int64_t* cu_seqlens, int64_t N, int64_t B, int64_t T, int64_t H, int64_t K, int64_t V) {
+  if (!q || !k || !v || !g || !beta || !out || !A_log || !dt_bias) return KDA_ERR_NULL;
+  if (K != kda::KD || V != kda::VD) return KDA_ERR_SHAPE;
+  if (B < 1 || T < 0 || H < 1 || H > (1 << 20)) return KDA_ERR_SHAPE;
+  if (cu_seqlens && (B != 1 || N < 1)) return KDA_ERR_SHAPE;
+  if (B * T >= (int64_t)INT32_MAX / 2) return KDA_ERR_SHAPE;
+  const int64_t nseq = cu_seqlens ? N : B;
+  if (nseq * H >= (int64_t)INT32_MAX / 256) return KDA_ERR_SHAPE;
+  auto bad_code = [](int c) { return c != KDA_STATE_NONE && c != KDA_STATE_BF16 && c != KDA_STATE_FP32; };
+  if (bad_code(initial_dtype) || bad_code(final_dtype)) return KDA_ERR_DTYPE;
+  if ((initial_dtype == KDA_STATE_NONE) != (initial_state == nullptr))
+    return initial_state ? KDA_ERR_DTYPE : KDA_ERR_NULL;
+  if ((final_dtype == KDA_STATE_NONE) != (final_state == nullptr)) return final_state ? KDA_ERR_DTYPE : KDA_ERR_NULL;
+  if (initial_state && final_state && initial_dtype != final_dtype) return KDA_ERR_DTYPE;
+  if (!std::isfinite(lower_bound) || lower_bound < -5.0f || lower_bound > 0.0f) return KDA_ERR_VALUE;
+  if (!std::isfinite(scale)) return KDA_ERR_VALUE;
+  const void* a16[] = {q, k, v, g, out, A_log, dt_bias};
+  for (const void* p : a16)
+    if (!aligned(p, 16)) return KDA_ERR_ALIGN;
+  if (!aligned(beta, 2)) return KDA_ERR_ALIGN;
+  if (initial_state && !aligned(initial_state, 16)) return KDA_ERR_ALIGN;
+  if (final_state && !aligned(final_state, 16)) return KDA_ERR_ALIGN;
+  if (cu_seqlens && !aligned(cu_seqlens, 8)) return KDA_ERR_ALIGN;
+  return KDA_OK;
+}
+
+int validate_cu_on_host(const int64_t* cu, int64_t N, int64_t T, hipStream_t stream) {
+  if (hipStreamSynchronize(stream) != hipSuccess) return KDA_ERR_HIP;
+  std::vector<int64_t> h((size_t)N + 1);
+  if (hipMemcpy(h.data(), cu, sizeof(int64_t) * (size_t)(N + 1), hipMemcpyDeviceToHost) != hipSuccess)
+    return KDA_ERR_HIP;
+  if (h[0] != 0 || h[(size_t)N] != T) return KDA_ERR_VALUE;
+  for (int64_t i = 0; i < N; ++i)
+    if (h[(size_t)i + 1] < h[(size_t)i]) return KDA_ERR_VALUE;
+  return KDA_OK;
+}
+
+kda::FwdParams make_params(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                           float scale, void* out, const float* A_log, const float* dt_bias, float lower_bound,
+                           const void* initial_state, int initial_dtype, void* final_state, int final_dtype,
+                           int64_t H) {
+  kda::FwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.g = static_cast<const uint16_t*>(g);
+  p.beta = static_cast<const uint16_t*>(beta);
+  p.out = static_cast<uint16_t*>(out);
+  p.A_log = A_log;
+  p.dt_bias = dt_bias;
+  p.init_state = initial_state;
+  p.final_state = final_state;
+  p.init_dtype = initial_dtype;
+  p.final_dtype = final_dtype;
+  p.scale = scale;
+  p.lower_bound = lower_bound;
+  p.H = (int32_t)H;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N) {
+  Layout L;
+  if (!make_layout(B, T, H, N, N > 0, L)) return 0;
+  return L.total;
+}
+
+int kda_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale, void* out,
+            const float* A_log, const float* dt_bias, float lower_bound, const void* initial_state,
+            int initial_dtype, void* final_state, int final_dtype, const int64_t* cu_seqlens, int64_t N, int64_t B,
+            int64_t T, int64_t H, int64_t K, int64_t V, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state, initial_dtype,
+                        final_state, final_dtype, cu_seqlens, N, B, T, H, K, V);
+  if (rc != KDA_OK) return rc;
+  const bool varlen = cu_seqlens != nullptr;
+  Layout L;
+  if (!make_layout(B, T, H, varlen ? N : 0, varlen, L)) return KDA_ERR_SHAPE;
+  if (L.total > 0) {
+    if (!workspace || workspace_bytes < L.total) return KDA_ERR_WORKSPACE;
+    if (!aligned(workspace, ALIGN)) return KDA_ERR_ALIGN;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (varlen && env_flag("KDA_VALIDATE")) {
+    rc = validate_cu_on_host(cu_seqlens, N, T, st);
+    if (rc != KDA_OK) return rc;
+  }
+
+  kda::FwdParams p = make_params(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                                 initial_dtype, final_state, final_dtype, H);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  p.rec = ws + L.rec;
+  p.map.T = (int32_t)T;
+  p.map.max_chunks = (int32_t)L.max_chunks;
+  p.map.nseq = (int32_t)(varlen ? N : B);
+  p.map.nc_row = (int32_t)((T + kda::CH - 1) / kda::CH);
+  if (varlen) {
+    p.map.seq_tab = reinterpret_cast<const int2*>(ws + L.seq_tab);
+    p.map.chunk_tab = reinterpret_cast<const int2*>(ws + L.chunk_tab);
+  }
+  if (env_flag("KDA_LOG"))
+    std::fprintf(stderr, "[kda] fwd B=%lld T=%lld H=%lld N=%lld chunks=%lld workspace=%zu varlen=%d\n",
+                 (long long)B, (long long)T, (long long)H, (long long)N, (long long)L.max_chunks, L.total,
+                 (int)varlen);
+
+  hipError_t e = hipSuccess;
+  if (varlen && L.max_chunks > 0)
+    e = kda::launch_sched(cu_seqlens, (int32_t)N, (int32_t)T, (int32_t)L.max_chunks,
+                          reinterpret_cast<int2*>(ws + L.seq_tab), reinterpret_cast<int2*>(ws + L.chunk_tab),
+                          reinterpret_cast<int32_t*>(ws + L.seq_start), st);
+  if (e == hipSuccess) e = kda::launch_intra(p, st);
+  if (e == hipSuccess) e = kda::launch_chain(p, st);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_fwd_recurrent(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,
+                      void* out, const float* A_log, const float* dt_bias, float lower_bound,
+                      const void* initial_state, int initial_dtype, void* final_state, int final_dtype,
+                      const int64_t* cu_seqlens, int64_t N, int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                      void* stream) {
+  int rc = check_common(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state, initial_dtype,
+                        final_state, final_dtype, cu_seqlens, N, B, T, H, K, V);
+  if (rc != KDA_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool varlen = cu_seqlens != nullptr;
+  if (varlen && env_flag("KDA_VALIDATE")) {
+    rc = validate_cu_on_host(cu_seqlens, N, T, st);
+    if (rc != KDA_OK) return rc;
+  }
+  kda::FwdParams p = make_params(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                                 initial_dtype, final_state, final_dtype, H);
+  p.map.T = (int32_t)T;
+  p.map.nseq = (int32_t)(varlen ? N : B);
+  hipError_t e = kda::launch_recurrent(p, cu_seqlens, st);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+const char* kda_status_string(int status) {
+  switch (status) {
+    case KDA_OK: return "KDA_OK: success";
+    case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE: unsupported or inconsistent sizes (K = V = 128, B = 1 with cu_seqlens)";
+    case KDA_ERR_DTYPE: return "KDA_ERR_DTYPE: unknown state dtype or initial/final state dtypes differ";
+    case KDA_ERR_VALUE: return "KDA_ERR_VALUE: lower_bound outside [-5, 0], non-finite scale, or bad cu_seqlens";
+    case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: pointer not aligned (16 bytes; workspace 256 bytes)";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or smaller than kda_fwd_workspace_size";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP runtime or kernel launch error";
+    default: return "KDA: unknown status";
+  }
+}
+
+const char* kda_version(void) { return "0.1.0 gfx950"; }
+
+}  // extern "C"

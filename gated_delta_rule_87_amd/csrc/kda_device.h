@@ -1,0 +1,108 @@
+// kda_device.h -- device-side building blocks shared by the gfx950 KDA kernels:
+// vector types, MFMA wrappers, bf16/fp16 packing, DPP scans, wave reductions,
+// and the workspace layout of the per-chunk intermediates.
+//
+// MFMA fragment conventions (v_mfma_f32_16x16x32_{bf16,f16}, wave64):
+//   A operand: lane l holds row (l & 15) and 8 contraction indices chosen by
+//              the lane group (l >> 4);
+//   B operand: lane l holds column (l & 15) and the same 8 contraction indices
+//              for lane group (l >> 4);
+//   D (4 fp32): lane l holds D[4*(l >> 4) + j][l & 15], j = 0..3.
+// Because A and B use the same lane-group -> contraction-index assignment, any
+// fixed permutation of the contraction index is allowed. The kernels use the
+// "D-compatible" order: within a 32-wide contraction step s, lane group gq
+// holds indices 32s + {4gq..4gq+3} (e = 0..3) and 32s + 16 + {4gq..4gq+3}
+// (e = 4..7). With that order the D registers of two vertically adjacent 16x16
+// tiles are exactly an operand fragment of a following product, so chains of
+// products need no transposes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int KD = 128;      // key dim K (fixed)
+constexpr int VD = 128;      // value dim V (fixed)
+constexpr int CH = 64;       // chunk length
+constexpr int SUB = 16;      // sub-chunk length (one wave's rows in the intra kernel)
+
+// ---- per-chunk-head intermediate record written by the intra kernel -------
+// All fragments are 64 lanes x 16 bytes = 1 KiB, stored in lane order.
+constexpr int FRAG = 1024;
+constexpr int OFF_WNEG = 0;                       // f16  [4 tok-tile][4 k-step]  : -W
+constexpr int OFF_QG = OFF_WNEG + 16 * FRAG;      // f16  [4 tok-tile][4 k-step]  : Q^.Gamma
+constexpr int OFF_KP = OFF_QG + 16 * FRAG;        // f16  [8 chan-tile][2 k-step] : K'^T
+constexpr int OFF_AQK = OFF_KP + 16 * FRAG;       // f16  [4 tok-tile][2 k-step]  : Aqk
+constexpr int OFF_UT = OFF_AQK + 8 * FRAG;        // f32  [8 v-tile][4 tok-tile][64][4] : U~
+constexpr int OFF_GAML = OFF_UT + 32 * FRAG;      // f32  [128] : exp(G_L)
+constexpr int REC_BYTES = OFF_GAML + 512;         // 90624 bytes per chunk and head
+
+// ---- small helpers ---------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// round-to-nearest-even fp32 -> bf16 (hardware v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  __bf16 x = (__bf16)a, y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+__device__ __forceinline__ uint16_t to_bf16(float a) { return __builtin_bit_cast(uint16_t, (__bf16)a); }
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  _Float16 x = (_Float16)a, y = (_Float16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+__device__ __forceinline__ uint16_t to_f16(float a) { return __builtin_bit_cast(uint16_t, (_Float16)a); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 u) { return __builtin_bit_cast(f16x8, u); }
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a), as_f16x8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float sigmoidf_fast(float x) { return fast_rcp(1.0f + fast_exp(-x)); }
+
+// Inclusive prefix sum across the 16 lanes of each DPP row (lane & 15 is the
+// position in the row). Row-shift DPP with bound_ctrl yields 0 past the row
+// start, so lanes with fewer predecessors add zeros.
+__device__ __forceinline__ float row16_inclusive_scan(float v) {
+  int x = __float_as_int(v);
+  float s = v;
+  s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x111, 0xf, 0xf, true));
+  s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x112, 0xf, 0xf, true));
+  s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x114, 0xf, 0xf, true));
+  s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x118, 0xf, 0xf, true));
+  (void)x;
+  return s;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Power-of-two scale s and its inverse such that max|x| * s lies in [1, 2).
+// The exponent is clamped so that both stay normal fp32 numbers; max|x| = 0
+// gives an arbitrary (harmless) scale because every scaled value is then 0.
+__device__ __forceinline__ void pow2_scale(float m, float& s, float& inv) {
+  int e = (int)((__float_as_uint(m) >> 23) & 0xff);   // biased exponent
+  e = e < 27 ? 27 : (e > 227 ? 227 : e);
+  s = __uint_as_float((uint32_t)(254 - e) << 23);
+  inv = __uint_as_float((uint32_t)e << 23);
+}
+
+}  // namespace kda

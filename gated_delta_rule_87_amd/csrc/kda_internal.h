@@ -1,0 +1,47 @@
+// kda_internal.h -- host-side launch interface between the C ABI (kda_api.cpp)
+// and the kernels (kda_*.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Where a chunk's tokens are: fixed-length rows (B rows of T tokens, chunk i is
+// row i / nc_row, piece i % nc_row) or the varlen tables built on the device.
+struct ChunkMap {
+  const int2* chunk_tab;   // varlen: [max_chunks] {t0, len}; len = 0 -> unused slot
+  const int2* seq_tab;     // varlen: [N] {first chunk, number of chunks}
+  int32_t T;               // tokens per row (fixed) / packed total (varlen)
+  int32_t nc_row;          // chunks per row (fixed)
+  int32_t max_chunks;      // number of chunk slots
+  int32_t nseq;            // sequences (B or N)
+};
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* g;
+  const uint16_t* beta;
+  uint16_t* out;
+  const float* A_log;
+  const float* dt_bias;
+  const void* init_state;
+  void* final_state;
+  int init_dtype;          // 0 none, 1 bf16, 2 fp32
+  int final_dtype;
+  float scale;
+  float lower_bound;
+  int32_t H;
+  ChunkMap map;
+  uint8_t* rec;            // chunk records: [max_chunks][H][REC_BYTES]
+};
+
+hipError_t launch_sched(const int64_t* cu_seqlens, int32_t N, int32_t T, int32_t max_chunks,
+                        int2* seq_tab, int2* chunk_tab, int32_t* seq_start, hipStream_t stream);
+hipError_t launch_intra(const FwdParams& p, hipStream_t stream);
+hipError_t launch_chain(const FwdParams& p, hipStream_t stream);
+hipError_t launch_recurrent(const FwdParams& p, const int64_t* cu_seqlens, hipStream_t stream);
+
+}  // namespace kda

@@ -1,0 +1,106 @@
+// kda_sched.hip -- varlen work scheduler of the chunked KDA forward (gfx950).
+//
+// From the packed cu_seqlens (int64 [N+1], B = 1, T = total length; "Kernel
+// API" table of the FlashKDA README digest) build, on the device and without
+// a host round trip:
+//   seq_tab[n]   = {first chunk index, number of 64-token chunks} of sequence n
+//   chunk_tab[i] = {first token, length <= 64} of chunk i (length 0: unused)
+// Chunks never straddle sequences; a sequence's last chunk may be partial.
+// Every sequence is clamped into [0, T] and the chunk count into the slot
+// budget floor(T/64) + N, so malformed contents cannot drive the other kernels
+// out of bounds (results are then unspecified, never a fault).
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int SCHED_THREADS = 1024;
+
+__global__ __launch_bounds__(SCHED_THREADS) void kda_sched_kernel(const int64_t* cu, int32_t N, int32_t T,
+                                                                  int32_t max_chunks, int2* seq_tab,
+                                                                  int2* chunk_tab, int32_t* seq_start) {
+  __shared__ int32_t warp_sums[SCHED_THREADS / 64];
+  __shared__ int32_t carry_s;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  if (tid == 0) carry_s = 0;
+  __syncthreads();
+
+  // pass 1: clamped lengths, chunk counts, exclusive scan of the counts
+  for (int base = 0; base < N; base += SCHED_THREADS) {
+    const int n = base + tid;
+    int32_t s = 0, len = 0, nc = 0;
+    if (n < N) {
+      int64_t a = cu[n], b = cu[n + 1];
+      a = a < 0 ? 0 : (a > T ? T : a);
+      b = b < a ? a : (b > T ? T : b);
+      s = (int32_t)a;
+      len = (int32_t)(b - a);
+      nc = (len + CH - 1) / CH;
+    }
+    // inclusive scan of nc within the wave, then across waves
+    int32_t x = nc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) warp_sums[wid] = x;
+    __syncthreads();
+    int32_t woff = 0;
+    for (int k = 0; k < wid; ++k) woff += warp_sums[k];
+    const int32_t carry = carry_s;
+    const int32_t first = carry + woff + x - nc;
+    if (n < N) {
+      const int32_t f = first < max_chunks ? first : max_chunks;
+      const int32_t cnt = nc < max_chunks - f ? nc : max_chunks - f;
+      seq_tab[n] = make_int2(f, cnt);
+      seq_start[n] = s;
+    }
+    __syncthreads();
+    if (tid == SCHED_THREADS - 1) carry_s = carry + woff + x;
+    __syncthreads();
+  }
+  __threadfence_block();
+  __syncthreads();
+
+  // pass 2: every chunk slot finds its sequence by binary search over seq_tab
+  for (int i = tid; i < max_chunks; i += SCHED_THREADS) {
+    int lo = 0, hi = N - 1, found = -1;
+    while (lo <= hi) {   // last n with seq_tab[n].x <= i
+      const int mid = (lo + hi) >> 1;
+      if (seq_tab[mid].x <= i) {
+        found = mid;
+        lo = mid + 1;
+      } else {
+        hi = mid - 1;
+      }
+    }
+    int2 e = make_int2(0, 0);
+    if (found >= 0) {
+      const int2 st = seq_tab[found];
+      const int jj = i - st.x;
+      if (jj < st.y) {
+        // length of the clamped sequence: recover from the chunk count and the next start
+        const int64_t a = seq_start[found];
+        int64_t b = cu[found + 1];
+        b = b < a ? a : (b > T ? T : b);
+        const int32_t len = (int32_t)(b - a);
+        const int32_t rem = len - jj * CH;
+        e = make_int2((int32_t)a + jj * CH, rem < CH ? rem : CH);
+      }
+    }
+    chunk_tab[i] = e;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_sched(const int64_t* cu_seqlens, int32_t N, int32_t T, int32_t max_chunks, int2* seq_tab,
+                        int2* chunk_tab, int32_t* seq_start, hipStream_t stream) {
+  hipLaunchKernelGGL(kda_sched_kernel, dim3(1), dim3(SCHED_THREADS), 0, stream, cu_seqlens, N, T, max_chunks,
+                     seq_tab, chunk_tab, seq_start);
+  return hipGetLastError();
+}
+
+}  // namespace kda

@@ -1,0 +1,141 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward library
+ * (libkda.so).
+ *
+ * The operation (per sequence n and head h, state S of V x K, K contiguous):
+ *   q^, k^ = L2-normalised q, k over K (x / sqrt(sum x^2 + 1e-6))
+ *   beta   = sigmoid(beta logit)
+ *   g~[c]  = lower_bound * sigmoid(exp(A_log[h]) * (g[c] + dt_bias[h][c]))
+ *   S      = S * Diag(exp(g~));  S = S - beta (S k^ - v) k^^T;  o = scale * S q^
+ * KDA is Gated DeltaNet with a per-channel gate (page "FlashKDA：基於 CUTLASS
+ * 的 Kimi Delta Attention CUDA 加速實作", section 背景). The pages print no
+ * equation; the gate form, natural exp, the 1e-6 epsilon and the order
+ * decay -> delta update -> read-out are this library's stated readings.
+ *
+ * The argument list mirrors flash_kda.fwd(q, k, v, g, beta, scale, out,
+ * A_log, dt_bias, lower_bound, initial_state, final_state, cu_seqlens) and its
+ * parameter table ("Kernel API" of the FlashKDA README digest, aiwatch.icu
+ * page), with the caller-owned, written-in-place `out` of the 2kiu.com guide
+ * (sections 一 and 三).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers (hipMalloc'd or from a caching
+ *     allocator), row-major and contiguous, aligned to 16 bytes (the state
+ *     and fp32 parameters to 16 bytes as well).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls are stream-ordered and asynchronous: they return as soon as the
+ *     work is enqueued. The library allocates nothing per call and keeps no
+ *     pointer after it returns; it is reentrant.
+ *   - Errors are detected on the host before anything is launched; on error
+ *     nothing is written. cu_seqlens CONTENTS live on the device and are a
+ *     caller precondition (cu[0] = 0, non-decreasing, cu[N] = T); the kernels
+ *     clamp every sequence into [0, T] so malformed contents cannot make them
+ *     access memory out of bounds (results are then unspecified). Setting the
+ *     environment variable KDA_VALIDATE=1 makes kda_fwd synchronise the stream
+ *     and check the contents on the host (KDA_ERR_VALUE if violated).
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,      /* a required pointer is NULL                           */
+    KDA_ERR_SHAPE = 2,     /* K != 128, V != 128, H < 1, T < 0, B < 1, B != 1 with
+                              cu_seqlens, N < 1 with cu_seqlens, size overflow      */
+    KDA_ERR_DTYPE = 3,     /* unknown state dtype code, or initial and final state
+                              given with different dtypes                           */
+    KDA_ERR_VALUE = 4,     /* lower_bound outside [-5, 0] or not finite, scale not
+                              finite, bad cu_seqlens contents (KDA_VALIDATE=1 only) */
+    KDA_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                      */
+    KDA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than kda_fwd_workspace_size */
+    KDA_ERR_HIP = 7        /* a HIP runtime call or kernel launch failed            */
+};
+
+/* State dtype codes for initial_state / final_state. */
+enum kda_state_dtype {
+    KDA_STATE_NONE = 0,    /* pointer must be NULL (stateless)  */
+    KDA_STATE_BF16 = 1,    /* bfloat16, rounded to nearest-even */
+    KDA_STATE_FP32 = 2     /* float32                           */
+};
+
+/*
+ * kda_fwd_workspace_size -- bytes of device workspace kda_fwd needs.
+ *   B, T, H: as for kda_fwd;  N: number of sequences when cu_seqlens is used,
+ *   0 otherwise. Returns 0 for invalid sizes (B < 1, T < 0, H < 1, N < 0).
+ * The workspace holds the per-chunk intermediates of the chunked (WY) form
+ * (about 88.5 KiB per 64-token chunk and head) and the varlen chunk tables.
+ */
+size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N);
+
+/*
+ * kda_fwd -- chunked KDA prefill forward (64-token chunks).
+ *
+ *   q, k, g      bf16 [B, T, H, K]   query, key, gate before activation
+ *   v            bf16 [B, T, H, V]   value
+ *   beta         bf16 [B, T, H]      beta logits (sigmoid applied inside)
+ *   scale        float               read-out scaling factor (finite)
+ *   out          bf16 [B, T, H, V]   OUTPUT, written in place; every element
+ *                                    is written, none is read (no need to
+ *                                    pre-zero it)
+ *   A_log        fp32 [H]            log-gate parameter
+ *   dt_bias      fp32 [H, K]         gate bias
+ *   lower_bound  float in [-5, 0]    gate lower bound
+ *   initial_state, initial_dtype     NULL/KDA_STATE_NONE (zeros) or
+ *                                    [B|N, H, V, K] bf16/fp32
+ *   final_state, final_dtype         NULL/KDA_STATE_NONE (not written) or
+ *                                    [B|N, H, V, K] bf16/fp32, written for every
+ *                                    (sequence, head), zero-length sequences
+ *                                    included. May alias initial_state.
+ *   cu_seqlens   int64 [N+1] or NULL packed sequence boundaries; requires
+ *                                    B == 1 and T the total packed length.
+ *                                    Without it, each of the B rows is an
+ *                                    independent sequence of length T.
+ *   N            number of sequences (ignored without cu_seqlens)
+ *   B, T, H, K, V                    sizes; K and V must be 128
+ *   workspace, workspace_bytes       caller-owned device scratch of at least
+ *                                    kda_fwd_workspace_size(B, T, H, N) bytes,
+ *                                    256-byte aligned; its contents need no
+ *                                    initialisation and are clobbered
+ *   stream       hipStream_t as void*
+ * Returns a kda_status.
+ */
+int kda_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
+            float scale, void *out, const float *A_log, const float *dt_bias, float lower_bound,
+            const void *initial_state, int initial_dtype, void *final_state, int final_dtype,
+            const int64_t *cu_seqlens, int64_t N, int64_t B, int64_t T, int64_t H, int64_t K,
+            int64_t V, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_fwd_recurrent -- the same operation computed token by token (one
+ * workgroup per sequence and head, fp32 state in registers). Same arguments
+ * and rules as kda_fwd, without a workspace. It is the path for online
+ * generation with state passing (decode-sized T; page "FlashKDA：面向SM90+的
+ * 高性能KDA CUDA内核库", Q2 on stateful/streaming use) and a reference for the
+ * chunked path on long inputs.
+ */
+int kda_fwd_recurrent(const void *q, const void *k, const void *v, const void *g,
+                      const void *beta, float scale, void *out, const float *A_log,
+                      const float *dt_bias, float lower_bound, const void *initial_state,
+                      int initial_dtype, void *final_state, int final_dtype,
+                      const int64_t *cu_seqlens, int64_t N, int64_t B, int64_t T, int64_t H,
+                      int64_t K, int64_t V, void *stream);
+
+/* kda_status_string -- static description of a status code (never NULL). */
+const char *kda_status_string(int status);
+
+/* kda_version -- library version string, e.g. "0.1.0 gfx950". */
+const char *kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */
