@@ -26,10 +26,10 @@ inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
   int64_t max_chunks = 0;
-  size_t rec = 0, seq_tab = 0, chunk_tab = 0, seq_start = 0, total = 0;
+  size_t rec = 0, seq_tab = 0, chunk_tab = 0, seq_span = 0, total = 0;
 };
 
-// Workspace regions: chunk records | seq_tab | chunk_tab | seq_start.
+// Workspace regions: chunk records | seq_tab | chunk_tab | seq_span.
 bool make_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool varlen, Layout& L) {
   if (B < 1 || T < 0 || H < 1 || N < 0) return false;
   if (varlen) {
@@ -46,8 +46,8 @@ bool make_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool varlen, Layout
   off = align_up(off + (varlen ? (size_t)N * sizeof(int2) : 0));
   L.chunk_tab = off;
   off = align_up(off + (varlen ? (size_t)L.max_chunks * sizeof(int2) : 0));
-  L.seq_start = off;
-  off = align_up(off + (varlen ? (size_t)N * sizeof(int32_t) : 0));
+  L.seq_span = off;
+  off = align_up(off + (varlen ? (size_t)N * sizeof(int2) : 0));
   L.total = off;
   return true;
 }
@@ -164,6 +164,7 @@ int kda_fwd(const void* q, const void* k, const void* v, const void* g, const vo
   if (varlen) {
     p.map.seq_tab = reinterpret_cast<const int2*>(ws + L.seq_tab);
     p.map.chunk_tab = reinterpret_cast<const int2*>(ws + L.chunk_tab);
+    p.map.seq_span = reinterpret_cast<const int2*>(ws + L.seq_span);
   }
   if (env_flag("KDA_LOG"))
     std::fprintf(stderr, "[kda] fwd B=%lld T=%lld H=%lld N=%lld chunks=%lld workspace=%zu varlen=%d\n",
@@ -174,7 +175,7 @@ int kda_fwd(const void* q, const void* k, const void* v, const void* g, const vo
   if (varlen && L.max_chunks > 0)
     e = kda::launch_sched(cu_seqlens, (int32_t)N, (int32_t)T, (int32_t)L.max_chunks,
                           reinterpret_cast<int2*>(ws + L.seq_tab), reinterpret_cast<int2*>(ws + L.chunk_tab),
-                          reinterpret_cast<int32_t*>(ws + L.seq_start), st);
+                          reinterpret_cast<int2*>(ws + L.seq_span), st);
   if (e == hipSuccess) e = kda::launch_intra(p, st);
   if (e == hipSuccess) e = kda::launch_chain(p, st);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;

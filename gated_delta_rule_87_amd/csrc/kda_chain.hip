@@ -1,179 +1,277 @@
 // kda_chain.hip -- inter-chunk state chain + output of the chunked KDA forward
 // (gfx950).
 //
-// One wave per (sequence, head, 16-wide value slice); a workgroup holds NW such
-// waves. Rows v of the state only ever meet column v of V and U, so value
-// slices are independent chains. Each wave keeps its 16 x 128 slice of the
-// fp32 state in registers for the whole sequence and walks the chunks in
-// order; per chunk (records written by the intra kernel):
-//     U      = U~ - W S0^T                            (16x128 . 128x16 per tile)
+// One workgroup per (sequence, head, group of NW*VT*16 value columns); wave w
+// owns VT 16-wide value tiles. Rows v of the state only ever meet column v of
+// V and U, so value slices are independent chains. Each wave keeps its slice
+// of the fp32 state in registers for the whole sequence and walks the chunks
+// in order; per chunk (records written by the intra kernel):
+//     U      = U~ - W S0^T
 //     O^T    = scale (S0 (Q^.Gamma)^T + U^T Aqk^T)     -> out (bf16), every row t < L
 //     S1^T   = Diag(Gamma_L) S0^T + K'^T U
-// with the state written to final_state after the last chunk. This is the
+// and the state goes to final_state after the last chunk. This is the
 // recurrent "state passing" half of the forward; initial_state/final_state
 // follow the "Kernel API" table of the FlashKDA README digest ([B|N,H,V,K],
 // bf16 or fp32, dtypes equal when both are given) and out is written once in
 // place (2kiu.com guide, section 二).
 //
+// Memory pipeline: everything a chunk step reads -- the 56 fragments shared by
+// all value tiles (-W, Qg, K'^T, Aqk: 56 KiB, contiguous at the start of the
+// record), each wave's U~ fragments and Gamma_L -- is copied one chunk ahead
+// into a two-deep LDS ring with direct global->LDS loads (no VGPR staging).
+// Waits are explicit vmcnt counts with bare s_barrier, so the prefetch of chunk
+// j+1 stays in flight while chunk j computes.
+//
 // Precision: MFMA operands are fp16. The state and U are scaled per 16-wide
-// slice by a power of two (max |x| * s in [1, 2)) before rounding, so fp16's
-// range is never exceeded and the scale is exact; accumulation is fp32.
+// tile by a power of two (max |x| * s in [1, 2)) before rounding, so fp16's
+// range is never exceeded and the scaling is exact; accumulation is fp32.
 #include "kda_device.h"
 #include "kda_internal.h"
+
+#ifndef KDA_CHAIN_NW
+#define KDA_CHAIN_NW 2
+#endif
+#ifndef KDA_CHAIN_VT
+#define KDA_CHAIN_VT 1
+#endif
 
 namespace kda {
 namespace {
 
-template <int NW>
+constexpr int NSHARED = 56;   // fragments per chunk shared by all value tiles
+
+#define LDSPTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt vmcnt(n) with expcnt/lgkmcnt left unconstrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
+__device__ __forceinline__ float tile_absmax(const f32x4* x, int n) {
+  float m = 0.0f;
+  for (int i = 0; i < n; ++i) m = fmaxf(m, fmaxf(fmaxf(fabsf(x[i].x), fabsf(x[i].y)), fmaxf(fabsf(x[i].z), fabsf(x[i].w))));
+  return wave_max(m);
+}
+
+__device__ __forceinline__ u32x4 pack_pair_f16(f32x4 a, f32x4 b, float s) {
+  a *= s;
+  b *= s;
+  return u32x4{pack_f16x2(a.x, a.y), pack_f16x2(a.z, a.w), pack_f16x2(b.x, b.y), pack_f16x2(b.z, b.w)};
+}
+
+template <int NW, int VT>
+struct ChainSmem {
+  u32x4 shared[NSHARED][64];     // -W, Qg, K'^T, Aqk fragments of the chunk (all value tiles)
+  f32x4 ut[NW][VT][4][64];       // U~ of each wave's value tiles
+  float gam[NW][KD];             // Gamma_L (one copy per wave: every wave loads its own)
+};
+
+template <int NW, int VT>
 __global__ __launch_bounds__(NW * 64) void kda_chain_kernel(FwdParams p, int nvg) {
+  __shared__ ChainSmem<NW, VT> ring[2];
+
   const int H = p.H;
   const int NH = p.map.nseq * H;
-  // blocks of the same (sequence, head) share blockIdx % 8, i.e. one XCD and its L2
+  // workgroups of one (sequence, head) share blockIdx % 8, i.e. one XCD and its L2
   const int id = blockIdx.x;
   const int xcd = id & 7, rest = id >> 3;
   const int vg = rest % nvg, grp = rest / nvg;
   const int nh = grp * 8 + xcd;
-  if (nh >= NH) return;
+  if (nh >= NH) return;   // uniform over the block
   const int n = nh / H, h = nh - n * H;
 
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, lt = l & 15, gq = l >> 4;
-  const int vt = vg * NW + w;          // 16-wide value tile
-  const int v = 16 * vt + lt;          // this lane's state row
+  const int vt0 = (vg * NW + w) * VT;   // first 16-wide value tile of this wave
 
-  int c0, nc;
+  int c0, nc, tok0, len;
   if (p.map.seq_tab) {
     const int2 e = p.map.seq_tab[n];
+    const int2 sp = p.map.seq_span[n];
     c0 = e.x;
     nc = e.y;
+    tok0 = sp.x;
+    len = sp.y;
   } else {
     c0 = n * p.map.nc_row;
     nc = p.map.nc_row;
+    tok0 = n * p.map.T;
+    len = p.map.T;
   }
 
-  // state slice, D layout of S^T: S[mt][j] = S[v][16mt + 4gq + j]
-  f32x4 S[8];
-  const size_t st_off = ((size_t)(n * H + h) * VD + v) * KD;
-  if (p.init_dtype == 2) {
-    const float* src = static_cast<const float*>(p.init_state) + st_off;
+  // state slices, D layout of S^T: S[t][mt][j] = S[16(vt0+t) + lt][16mt + 4gq + j]
+  f32x4 S[VT][8];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) S[mt] = *reinterpret_cast<const f32x4*>(src + 16 * mt + 4 * gq);
-  } else if (p.init_dtype == 1) {
-    const uint16_t* src = static_cast<const uint16_t*>(p.init_state) + st_off;
+  for (int t = 0; t < VT; ++t) {
+    const size_t st_off = ((size_t)(n * H + h) * VD + 16 * (vt0 + t) + lt) * KD;
+    if (p.init_dtype == 2) {
+      const float* src = static_cast<const float*>(p.init_state) + st_off;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      const u32x2 r = *reinterpret_cast<const u32x2*>(src + 16 * mt + 4 * gq);
-      S[mt] = f32x4{bf16_lo(r.x), bf16_hi(r.x), bf16_lo(r.y), bf16_hi(r.y)};
+      for (int mt = 0; mt < 8; ++mt) S[t][mt] = *reinterpret_cast<const f32x4*>(src + 16 * mt + 4 * gq);
+    } else if (p.init_dtype == 1) {
+      const uint16_t* src = static_cast<const uint16_t*>(p.init_state) + st_off;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const u32x2 r = *reinterpret_cast<const u32x2*>(src + 16 * mt + 4 * gq);
+        S[t][mt] = f32x4{bf16_lo(r.x), bf16_hi(r.x), bf16_lo(r.y), bf16_hi(r.y)};
+      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) S[t][mt] = f32x4{0, 0, 0, 0};
     }
-  } else {
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0, 0, 0, 0};
   }
+  wait_vmcnt<0>();   // the loop below then carries no pending register loads
 
+  // one prefetch = NSHARED/NW shared fragments + 4*VT U~ fragments + Gamma_L, all straight into LDS
+  auto prefetch = [&](int j, int buf) {
+    const uint8_t* rec = p.rec + ((size_t)(c0 + j) * H + h) * REC_BYTES;
+#pragma unroll
+    for (int i = 0; i < NSHARED / NW; ++i) {
+      const int f = i * NW + w;
+      __builtin_amdgcn_global_load_lds(rec + f * FRAG + l * 16, LDSPTR(&ring[buf].shared[f][0]), 16, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < VT; ++t)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        __builtin_amdgcn_global_load_lds(rec + OFF_UT + ((vt0 + t) * 4 + mt) * FRAG + l * 16,
+                                         LDSPTR(&ring[buf].ut[w][t][mt][0]), 16, 0, 0);
+    if (l < 32)
+      __builtin_amdgcn_global_load_lds(rec + OFF_GAML + l * 16, LDSPTR(&ring[buf].gam[w][0]), 16, 0, 0);
+  };
+  constexpr int KPF = NSHARED / NW + 4 * VT + 1;   // vector-memory ops issued per prefetch
+
+  if (nc > 0) prefetch(0, 0);
   const float scale = p.scale;
   for (int j = 0; j < nc; ++j) {
-    const int ci = c0 + j;
-    int t0, L;
-    if (p.map.chunk_tab) {
-      const int2 e = p.map.chunk_tab[ci];
-      t0 = e.x;
-      L = e.y;
+    const int b = j & 1;
+    __builtin_amdgcn_s_barrier();            // everyone is done with the buffer we refill next
+    if (j + 1 < nc) {
+      prefetch(j + 1, b ^ 1);
+      wait_vmcnt<KPF>();                       // chunk j's loads (issued earlier) have landed
     } else {
-      t0 = n * p.map.T + j * CH;
-      L = min(CH, p.map.T - j * CH);
+      wait_vmcnt<0>();
     }
-    const uint8_t* rec = p.rec + ((size_t)ci * H + h) * REC_BYTES;
-    auto frag = [&](int off, int f) { return *reinterpret_cast<const u32x4*>(rec + off + (f * 64 + l) * 16); };
+    __builtin_amdgcn_s_barrier();            // ... for every wave of the block
+    const ChainSmem<NW, VT>& R = ring[b];
+    const int t0 = tok0 + j * CH;
+    const int L = min(CH, len - j * CH);
 
-    // scale the state slice into fp16 operand fragments (k-step s: channel tiles 2s, 2s+1)
-    float m = 0.0f;
+    // state -> scaled fp16 operand fragments (k-step s: channel tiles 2s, 2s+1)
+    float sS[VT], iS[VT];
+    u32x4 sf[VT][4];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-      m = fmaxf(m, fmaxf(fmaxf(fabsf(S[mt].x), fabsf(S[mt].y)), fmaxf(fabsf(S[mt].z), fabsf(S[mt].w))));
-    m = wave_max(m);
-    float sS, iS;
-    pow2_scale(m, sS, iS);
-    u32x4 sf[4];
+    for (int t = 0; t < VT; ++t) {
+      pow2_scale(tile_absmax(S[t], 8), sS[t], iS[t]);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const f32x4 a = S[2 * s] * sS, b = S[2 * s + 1] * sS;
-      sf[s] = u32x4{pack_f16x2(a.x, a.y), pack_f16x2(a.z, a.w), pack_f16x2(b.x, b.y), pack_f16x2(b.z, b.w)};
+      for (int s = 0; s < 4; ++s) sf[t][s] = pack_pair_f16(S[t][2 * s], S[t][2 * s + 1], sS[t]);
     }
 
-    // U = U~ + (-W) S0^T       D layout: lane <-> v, registers <-> tokens 16mt + 4gq + j
-    f32x4 U[4];
+    // U = U~ + (-W) S0^T     D layout: lane <-> v, registers <-> tokens 16mt + 4gq + j
+    f32x4 U[VT][4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      f32x4 acc = {0, 0, 0, 0};
+      f32x4 acc[VT];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc = mfma_f16(frag(OFF_WNEG, mt * 4 + s), sf[s], acc);
-      const f32x4 ut = *reinterpret_cast<const f32x4*>(rec + OFF_UT + ((vt * 4 + mt) * 64 + l) * 16);
-      U[mt] = ut + acc * iS;
+      for (int t = 0; t < VT; ++t) acc[t] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 a = R.shared[mt * 4 + s][l];
+#pragma unroll
+        for (int t = 0; t < VT; ++t) acc[t] = mfma_f16(a, sf[t][s], acc[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < VT; ++t) U[t][mt] = R.ut[w][t][mt][l] + acc[t] * iS[t];
     }
-    float mu = 0.0f;
+    float sU[VT], iU[VT];
+    u32x4 uf[VT][2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-      mu = fmaxf(mu, fmaxf(fmaxf(fabsf(U[mt].x), fabsf(U[mt].y)), fmaxf(fabsf(U[mt].z), fabsf(U[mt].w))));
-    mu = wave_max(mu);
-    float sU, iU;
-    pow2_scale(mu, sU, iU);
-    u32x4 uf[2];
+    for (int t = 0; t < VT; ++t) {
+      pow2_scale(tile_absmax(U[t], 4), sU[t], iU[t]);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const f32x4 a = U[2 * s] * sU, b = U[2 * s + 1] * sU;
-      uf[s] = u32x4{pack_f16x2(a.x, a.y), pack_f16x2(a.z, a.w), pack_f16x2(b.x, b.y), pack_f16x2(b.z, b.w)};
+      for (int s = 0; s < 2; ++s) uf[t][s] = pack_pair_f16(U[t][2 * s], U[t][2 * s + 1], sU[t]);
     }
 
     // O^T = scale (S0 Qg^T + U^T Aqk^T)   D layout: lane <-> token 16nt + lt, registers <-> v
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      f32x4 aq = {0, 0, 0, 0}, aa = {0, 0, 0, 0};
+      f32x4 aq[VT], aa[VT];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) aq = mfma_f16(sf[s], frag(OFF_QG, nt * 4 + s), aq);
-      aa = mfma_f16(uf[0], frag(OFF_AQK, nt * 2), aa);
-      if (nt >= 2) aa = mfma_f16(uf[1], frag(OFF_AQK, nt * 2 + 1), aa);
-      const f32x4 o = (aq * iS + aa * iU) * scale;
-      const int t = 16 * nt + lt;
-      if (t < L) {
-        uint16_t* dst = p.out + ((size_t)(t0 + t) * H + h) * VD + 16 * vt + 4 * gq;
-        *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
+      for (int t = 0; t < VT; ++t) aq[t] = aa[t] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 qv = R.shared[16 + nt * 4 + s][l];
+#pragma unroll
+        for (int t = 0; t < VT; ++t) aq[t] = mfma_f16(sf[t][s], qv, aq[t]);
+      }
+      {
+        const u32x4 a0 = R.shared[48 + nt * 2][l];
+#pragma unroll
+        for (int t = 0; t < VT; ++t) aa[t] = mfma_f16(uf[t][0], a0, aa[t]);
+      }
+      if (nt >= 2) {
+        const u32x4 a1 = R.shared[48 + nt * 2 + 1][l];
+#pragma unroll
+        for (int t = 0; t < VT; ++t) aa[t] = mfma_f16(uf[t][1], a1, aa[t]);
+      }
+      const int tok = 16 * nt + lt;
+      if (tok < L) {
+        uint16_t* dst = p.out + ((size_t)(t0 + tok) * H + h) * VD + 4 * gq;
+#pragma unroll
+        for (int t = 0; t < VT; ++t) {
+          const f32x4 o = (aq[t] * iS[t] + aa[t] * iU[t]) * scale;
+          *reinterpret_cast<u32x2*>(dst + 16 * (vt0 + t)) = u32x2{pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
+        }
       }
     }
 
     // S1^T = Diag(Gamma_L) S0^T + K'^T U
-    const float* gam = reinterpret_cast<const float*>(rec + OFF_GAML);
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
-      f32x4 acc = {0, 0, 0, 0};
-      acc = mfma_f16(frag(OFF_KP, mt * 2), uf[0], acc);
-      acc = mfma_f16(frag(OFF_KP, mt * 2 + 1), uf[1], acc);
-      const f32x4 g4 = *reinterpret_cast<const f32x4*>(gam + 16 * mt + 4 * gq);
-      S[mt] = S[mt] * g4 + acc * iU;
+      const u32x4 k0 = R.shared[32 + mt * 2][l], k1 = R.shared[32 + mt * 2 + 1][l];
+      const f32x4 g4 = *reinterpret_cast<const f32x4*>(&R.gam[w][16 * mt + 4 * gq]);
+#pragma unroll
+      for (int t = 0; t < VT; ++t) {
+        f32x4 acc = {0, 0, 0, 0};
+        acc = mfma_f16(k0, uf[t][0], acc);
+        acc = mfma_f16(k1, uf[t][1], acc);
+        S[t][mt] = S[t][mt] * g4 + acc * iU[t];
+      }
     }
   }
 
-  if (p.final_dtype == 2) {
-    float* dst = static_cast<float*>(p.final_state) + st_off;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(dst + 16 * mt + 4 * gq) = S[mt];
-  } else if (p.final_dtype == 1) {
-    uint16_t* dst = static_cast<uint16_t*>(p.final_state) + st_off;
+  for (int t = 0; t < VT; ++t) {
+    const size_t st_off = ((size_t)(n * H + h) * VD + 16 * (vt0 + t) + lt) * KD;
+    if (p.final_dtype == 2) {
+      float* dst = static_cast<float*>(p.final_state) + st_off;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-      *reinterpret_cast<u32x2*>(dst + 16 * mt + 4 * gq) =
-          u32x2{pack_bf16x2(S[mt].x, S[mt].y), pack_bf16x2(S[mt].z, S[mt].w)};
+      for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(dst + 16 * mt + 4 * gq) = S[t][mt];
+    } else if (p.final_dtype == 1) {
+      uint16_t* dst = static_cast<uint16_t*>(p.final_state) + st_off;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+        *reinterpret_cast<u32x2*>(dst + 16 * mt + 4 * gq) =
+            u32x2{pack_bf16x2(S[t][mt].x, S[t][mt].y), pack_bf16x2(S[t][mt].z, S[t][mt].w)};
+    }
   }
 }
 
-constexpr int CHAIN_NW = 4;   // waves per workgroup (64 value columns)
+static_assert(NSHARED % KDA_CHAIN_NW == 0, "shared fragments must split evenly over the waves");
+static_assert(VD % (16 * KDA_CHAIN_NW * KDA_CHAIN_VT) == 0, "value tiles must split evenly");
+static_assert(OFF_QG == 16 * FRAG && OFF_KP == 32 * FRAG && OFF_AQK == 48 * FRAG,
+              "shared fragments must be contiguous at the record start");
 
 }  // namespace
 
 hipError_t launch_chain(const FwdParams& p, hipStream_t stream) {
   const int NH = p.map.nseq * p.H;
   if (NH <= 0) return hipSuccess;
-  const int nvg = VD / (16 * CHAIN_NW);
+  constexpr int NW = KDA_CHAIN_NW, VT = KDA_CHAIN_VT;
+  const int nvg = VD / (16 * NW * VT);
   const int64_t blocks = (int64_t)((NH + 7) / 8) * 8 * nvg;
-  hipLaunchKernelGGL(kda_chain_kernel<CHAIN_NW>, dim3((unsigned)blocks), dim3(CHAIN_NW * 64), 0, stream, p, nvg);
+  hipLaunchKernelGGL((kda_chain_kernel<NW, VT>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, p, nvg);
   return hipGetLastError();
 }
 

@@ -4,6 +4,7 @@
 // API" table of the FlashKDA README digest) build, on the device and without
 // a host round trip:
 //   seq_tab[n]   = {first chunk index, number of 64-token chunks} of sequence n
+//   seq_span[n]  = {first token, length} of sequence n (after clamping)
 //   chunk_tab[i] = {first token, length <= 64} of chunk i (length 0: unused)
 // Chunks never straddle sequences; a sequence's last chunk may be partial.
 // Every sequence is clamped into [0, T] and the chunk count into the slot
@@ -19,7 +20,7 @@ constexpr int SCHED_THREADS = 1024;
 
 __global__ __launch_bounds__(SCHED_THREADS) void kda_sched_kernel(const int64_t* cu, int32_t N, int32_t T,
                                                                   int32_t max_chunks, int2* seq_tab,
-                                                                  int2* chunk_tab, int32_t* seq_start) {
+                                                                  int2* chunk_tab, int2* seq_span) {
   __shared__ int32_t warp_sums[SCHED_THREADS / 64];
   __shared__ int32_t carry_s;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -55,7 +56,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void kda_sched_kernel(const int64_t*
       const int32_t f = first < max_chunks ? first : max_chunks;
       const int32_t cnt = nc < max_chunks - f ? nc : max_chunks - f;
       seq_tab[n] = make_int2(f, cnt);
-      seq_start[n] = s;
+      seq_span[n] = make_int2(s, len);
     }
     __syncthreads();
     if (tid == SCHED_THREADS - 1) carry_s = carry + woff + x;
@@ -81,13 +82,9 @@ __global__ __launch_bounds__(SCHED_THREADS) void kda_sched_kernel(const int64_t*
       const int2 st = seq_tab[found];
       const int jj = i - st.x;
       if (jj < st.y) {
-        // length of the clamped sequence: recover from the chunk count and the next start
-        const int64_t a = seq_start[found];
-        int64_t b = cu[found + 1];
-        b = b < a ? a : (b > T ? T : b);
-        const int32_t len = (int32_t)(b - a);
-        const int32_t rem = len - jj * CH;
-        e = make_int2((int32_t)a + jj * CH, rem < CH ? rem : CH);
+        const int2 sp = seq_span[found];
+        const int32_t rem = sp.y - jj * CH;
+        e = make_int2(sp.x + jj * CH, rem < CH ? rem : CH);
       }
     }
     chunk_tab[i] = e;
@@ -97,9 +94,9 @@ __global__ __launch_bounds__(SCHED_THREADS) void kda_sched_kernel(const int64_t*
 }  // namespace
 
 hipError_t launch_sched(const int64_t* cu_seqlens, int32_t N, int32_t T, int32_t max_chunks, int2* seq_tab,
-                        int2* chunk_tab, int32_t* seq_start, hipStream_t stream) {
+                        int2* chunk_tab, int2* seq_span, hipStream_t stream) {
   hipLaunchKernelGGL(kda_sched_kernel, dim3(1), dim3(SCHED_THREADS), 0, stream, cu_seqlens, N, T, max_chunks,
-                     seq_tab, chunk_tab, seq_start);
+                     seq_tab, chunk_tab, seq_span);
   return hipGetLastError();
 }
 
