@@ -41,28 +41,32 @@ class KDAError(RuntimeError):
         self.code = code
 
 
+def _setup(L):
+    """Declare the C signatures of include/kda.h on a loaded libkda.so."""
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    F = ctypes.c_float
+    L.kda_fwd_workspace_size.restype = ctypes.c_size_t
+    L.kda_fwd_workspace_size.argtypes = [I64, I64, I64, I64]
+    L.kda_fwd.restype = I
+    L.kda_fwd.argtypes = [P, P, P, P, P, F, P, P, P, F, P, I, P, I, P, I64, I64, I64, I64, I64, I64, P,
+                          ctypes.c_size_t, P]
+    L.kda_fwd_recurrent.restype = I
+    L.kda_fwd_recurrent.argtypes = [P, P, P, P, P, F, P, P, P, F, P, I, P, I, P, I64, I64, I64, I64, I64,
+                                    I64, P]
+    L.kda_status_string.restype = ctypes.c_char_p
+    L.kda_status_string.argtypes = [I]
+    L.kda_version.restype = ctypes.c_char_p
+    L.kda_version.argtypes = []
+    return L
+
+
 def lib():
     """Load libkda.so (built in-tree by gated_delta_rule_87_amd.build). Raises if missing."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"libkda.so not built ({LIB_PATH}); run python -m gated_delta_rule_87_amd.build")
-        L = ctypes.CDLL(LIB_PATH)
-        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-        F = ctypes.c_float
-        L.kda_fwd_workspace_size.restype = ctypes.c_size_t
-        L.kda_fwd_workspace_size.argtypes = [I64, I64, I64, I64]
-        L.kda_fwd.restype = I
-        L.kda_fwd.argtypes = [P, P, P, P, P, F, P, P, P, F, P, I, P, I, P, I64, I64, I64, I64, I64, I64, P,
-                              ctypes.c_size_t, P]
-        L.kda_fwd_recurrent.restype = I
-        L.kda_fwd_recurrent.argtypes = [P, P, P, P, P, F, P, P, P, F, P, I, P, I, P, I64, I64, I64, I64, I64,
-                                        I64, P]
-        L.kda_status_string.restype = ctypes.c_char_p
-        L.kda_status_string.argtypes = [I]
-        L.kda_version.restype = ctypes.c_char_p
-        L.kda_version.argtypes = []
-        _lib = L
+        _lib = _setup(ctypes.CDLL(LIB_PATH))
     return _lib
 
 

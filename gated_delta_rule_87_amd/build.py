@@ -24,9 +24,9 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
+def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [HIPCC, *FLAGS, *extra_flags, "-o", tmp, *[
         # hipcc treats .cpp as host C++ unless told otherwise; the API file is host-only
         s for s in srcs]]
@@ -41,8 +41,8 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         raise RuntimeError("hipcc failed building libkda.so")
     if verbose and err.strip():
         sys.stderr.write(err + "\n")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -22,9 +22,10 @@
 // Waits are explicit vmcnt counts with bare s_barrier, so the prefetch of chunk
 // j+1 stays in flight while chunk j computes.
 //
-// Precision: MFMA operands are fp16. The state and U are scaled per 16-wide
-// tile by a power of two (max |x| * s in [1, 2)) before rounding, so fp16's
-// range is never exceeded and the scaling is exact; accumulation is fp32.
+// Precision: MFMA operands are fp16. Each state row and each column of U is
+// scaled by its own power of two (max |x| * s in [1, 2)) before rounding, so
+// fp16's range is never exceeded and the scaling is exact; accumulation is
+// fp32.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -49,10 +50,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
-__device__ __forceinline__ float tile_absmax(const f32x4* x, int n) {
+// max |x| over one state row / U column: this lane's registers, then the four
+// lane groups that hold the other channels (tokens) of the same row (column)
+__device__ __forceinline__ float row_absmax(const f32x4* x, int n) {
   float m = 0.0f;
   for (int i = 0; i < n; ++i) m = fmaxf(m, fmaxf(fmaxf(fabsf(x[i].x), fabsf(x[i].y)), fmaxf(fabsf(x[i].z), fabsf(x[i].w))));
-  return wave_max(m);
+  return max_over_groups(m);
 }
 
 __device__ __forceinline__ u32x4 pack_pair_f16(f32x4 a, f32x4 b, float s) {
@@ -82,17 +85,18 @@ __global__ __launch_bounds__(NW * 64) void kda_chain_kernel(FwdParams p, int nvg
   if (nh >= NH) return;   // uniform over the block
   const int n = nh / H, h = nh - n * H;
 
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, lt = l & 15, gq = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, uniform
+  const int l = threadIdx.x & 63, lt = l & 15, gq = l >> 4;
   const int vt0 = (vg * NW + w) * VT;   // first 16-wide value tile of this wave
 
   int c0, nc, tok0, len;
   if (p.map.seq_tab) {
     const int2 e = p.map.seq_tab[n];
     const int2 sp = p.map.seq_span[n];
-    c0 = e.x;
-    nc = e.y;
-    tok0 = sp.x;
-    len = sp.y;
+    c0 = __builtin_amdgcn_readfirstlane(e.x);
+    nc = __builtin_amdgcn_readfirstlane(e.y);
+    tok0 = __builtin_amdgcn_readfirstlane(sp.x);
+    len = __builtin_amdgcn_readfirstlane(sp.y);
   } else {
     c0 = n * p.map.nc_row;
     nc = p.map.nc_row;
@@ -158,12 +162,13 @@ __global__ __launch_bounds__(NW * 64) void kda_chain_kernel(FwdParams p, int nvg
     const int t0 = tok0 + j * CH;
     const int L = min(CH, len - j * CH);
 
-    // state -> scaled fp16 operand fragments (k-step s: channel tiles 2s, 2s+1)
+    // state -> fp16 operand fragments (k-step s: channel tiles 2s, 2s+1), each state
+    // row v scaled by its own power of two
     float sS[VT], iS[VT];
     u32x4 sf[VT][4];
 #pragma unroll
     for (int t = 0; t < VT; ++t) {
-      pow2_scale(tile_absmax(S[t], 8), sS[t], iS[t]);
+      pow2_scale(row_absmax(S[t], 8), sS[t], iS[t]);
 #pragma unroll
       for (int s = 0; s < 4; ++s) sf[t][s] = pack_pair_f16(S[t][2 * s], S[t][2 * s + 1], sS[t]);
     }
@@ -188,12 +193,21 @@ __global__ __launch_bounds__(NW * 64) void kda_chain_kernel(FwdParams p, int nvg
     u32x4 uf[VT][2];
 #pragma unroll
     for (int t = 0; t < VT; ++t) {
-      pow2_scale(tile_absmax(U[t], 4), sU[t], iU[t]);
+      pow2_scale(row_absmax(U[t], 4), sU[t], iU[t]);
 #pragma unroll
       for (int s = 0; s < 2; ++s) uf[t][s] = pack_pair_f16(U[t][2 * s], U[t][2 * s + 1], sU[t]);
     }
 
-    // O^T = scale (S0 Qg^T + U^T Aqk^T)   D layout: lane <-> token 16nt + lt, registers <-> v
+    // O^T = scale (S0 Qg^T + U^T Aqk^T)   D layout: lane <-> token 16nt + lt, registers <-> v.
+    // Register j of lane group gq belongs to value row 4gq + j, whose scales live in lane 4gq + j.
+    f32x4 oS[VT], oU[VT];
+#pragma unroll
+    for (int t = 0; t < VT; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        oS[t][jj] = __shfl(iS[t], 4 * gq + jj, 64) * scale;
+        oU[t][jj] = __shfl(iU[t], 4 * gq + jj, 64) * scale;
+      }
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       f32x4 aq[VT], aa[VT];
@@ -220,7 +234,7 @@ __global__ __launch_bounds__(NW * 64) void kda_chain_kernel(FwdParams p, int nvg
         uint16_t* dst = p.out + ((size_t)(t0 + tok) * H + h) * VD + 4 * gq;
 #pragma unroll
         for (int t = 0; t < VT; ++t) {
-          const f32x4 o = (aq[t] * iS[t] + aa[t] * iU[t]) * scale;
+          const f32x4 o = aq[t] * oS[t] + aa[t] * oU[t];
           *reinterpret_cast<u32x2*>(dst + 16 * (vt0 + t)) = u32x2{pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
         }
       }

@@ -27,6 +27,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int KD = 128;      // key dim K (fixed)
 constexpr int VD = 128;      // value dim V (fixed)
@@ -55,9 +57,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 __device__ __forceinline__ uint16_t to_bf16(float a) { return __builtin_bit_cast(uint16_t, (__bf16)a); }
+// round-to-nearest-even fp32 pair -> packed fp16 (one v_cvt_pk_f16_f32 on gfx950)
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
-  _Float16 x = (_Float16)a, y = (_Float16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
 }
 __device__ __forceinline__ uint16_t to_f16(float a) { return __builtin_bit_cast(uint16_t, (_Float16)a); }
 
@@ -79,14 +81,21 @@ __device__ __forceinline__ float sigmoidf_fast(float x) { return fast_rcp(1.0f +
 // position in the row). Row-shift DPP with bound_ctrl yields 0 past the row
 // start, so lanes with fewer predecessors add zeros.
 __device__ __forceinline__ float row16_inclusive_scan(float v) {
-  int x = __float_as_int(v);
   float s = v;
   s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x111, 0xf, 0xf, true));
   s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x112, 0xf, 0xf, true));
   s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x114, 0xf, 0xf, true));
   s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x118, 0xf, 0xf, true));
-  (void)x;
   return s;
+}
+
+// max over the four lanes {l, l^16, l^32, l^48} (the lane groups sharing l & 15),
+// with the gfx950 cross-half lane swaps (no LDS round trip)
+__device__ __forceinline__ float max_over_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -107,7 +107,8 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
   if (L <= 0) return;   // unused varlen slot (uniform over the block)
   uint8_t* rec = p.rec + ((size_t)ci * H + h) * REC_BYTES;
 
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lt = l & 15, gq = l >> 4;
+  const int tid = threadIdx.x, l = tid & 63, lt = l & 15, gq = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index = sub-chunk, uniform
   const int tok = w * SUB + lt;
   const bool valid = tok < L;
   const size_t rowoff = ((size_t)(t0 + (valid ? tok : 0)) * H + h) * KD;
