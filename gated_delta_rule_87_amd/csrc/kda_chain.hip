@@ -17,7 +17,7 @@
 //
 // Memory pipeline: everything a chunk step reads -- the 56 fragments shared by
 // all value tiles (-W, Qg, K'^T, Aqk: 56 KiB, contiguous at the start of the
-// record), each wave's U~ fragments and Gamma_L -- is copied one chunk ahead
+// record), each wave's U~ tiles and scales, and Gamma_L -- is copied one chunk ahead
 // into a two-deep LDS ring with direct global->LDS loads (no VGPR staging).
 // Waits are explicit vmcnt counts with bare s_barrier, so the prefetch of chunk
 // j+1 stays in flight while chunk j computes.
@@ -67,7 +67,8 @@ __device__ __forceinline__ u32x4 pack_pair_f16(f32x4 a, f32x4 b, float s) {
 template <int NW, int VT>
 struct ChainSmem {
   u32x4 shared[NSHARED][64];     // -W, Qg, K'^T, Aqk fragments of the chunk (all value tiles)
-  f32x4 ut[NW][VT][4][64];       // U~ of each wave's value tiles
+  u32x2 ut[NW][VT][4][64];       // U~ (fp16, scaled) of each wave's value tiles [token tile][lane]
+  float usc[NW][VT][4][16];      // 1 / scale per (token tile, value column)
   float gam[NW][KD];             // Gamma_L (one copy per wave: every wave loads its own)
 };
 
@@ -136,15 +137,19 @@ __global__ __launch_bounds__(NW * 64) void kda_chain_kernel(FwdParams p, int nvg
       __builtin_amdgcn_global_load_lds(rec + f * FRAG + l * 16, LDSPTR(&ring[buf].shared[f][0]), 16, 0, 0);
     }
 #pragma unroll
-    for (int t = 0; t < VT; ++t)
+    for (int t = 0; t < VT; ++t) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        __builtin_amdgcn_global_load_lds(rec + OFF_UT + ((vt0 + t) * 4 + mt) * FRAG + l * 16,
-                                         LDSPTR(&ring[buf].ut[w][t][mt][0]), 16, 0, 0);
+      for (int hh = 0; hh < 2; ++hh)
+        __builtin_amdgcn_global_load_lds(rec + OFF_UT + (vt0 + t) * 2048 + hh * FRAG + l * 16,
+                                         LDSPTR(&ring[buf].ut[w][t][2 * hh][0]), 16, 0, 0);
+      if (l < 16)
+        __builtin_amdgcn_global_load_lds(rec + OFF_USC + (vt0 + t) * 256 + l * 16,
+                                         LDSPTR(&ring[buf].usc[w][t][0][0]), 16, 0, 0);
+    }
     if (l < 32)
       __builtin_amdgcn_global_load_lds(rec + OFF_GAML + l * 16, LDSPTR(&ring[buf].gam[w][0]), 16, 0, 0);
   };
-  constexpr int KPF = NSHARED / NW + 4 * VT + 1;   // vector-memory ops issued per prefetch
+  constexpr int KPF = NSHARED / NW + 3 * VT + 1;   // vector-memory ops issued per prefetch
 
   if (nc > 0) prefetch(0, 0);
   const float scale = p.scale;
@@ -187,7 +192,12 @@ __global__ __launch_bounds__(NW * 64) void kda_chain_kernel(FwdParams p, int nvg
         for (int t = 0; t < VT; ++t) acc[t] = mfma_f16(a, sf[t][s], acc[t]);
       }
 #pragma unroll
-      for (int t = 0; t < VT; ++t) U[t][mt] = R.ut[w][t][mt][l] + acc[t] * iS[t];
+      for (int t = 0; t < VT; ++t) {
+        const u32x2 uh = R.ut[w][t][mt][l];
+        const f32x2 u01 = __builtin_convertvector(__builtin_bit_cast(f16x2, uh.x), f32x2);
+        const f32x2 u23 = __builtin_convertvector(__builtin_bit_cast(f16x2, uh.y), f32x2);
+        U[t][mt] = f32x4{u01.x, u01.y, u23.x, u23.y} * R.usc[w][t][mt][lt] + acc[t] * iS[t];
+      }
     }
     float sU[VT], iU[VT];
     u32x4 uf[VT][2];

@@ -42,9 +42,10 @@ constexpr int OFF_WNEG = 0;                       // f16  [4 tok-tile][4 k-step]
 constexpr int OFF_QG = OFF_WNEG + 16 * FRAG;      // f16  [4 tok-tile][4 k-step]  : Q^.Gamma
 constexpr int OFF_KP = OFF_QG + 16 * FRAG;        // f16  [8 chan-tile][2 k-step] : K'^T
 constexpr int OFF_AQK = OFF_KP + 16 * FRAG;       // f16  [4 tok-tile][2 k-step]  : Aqk
-constexpr int OFF_UT = OFF_AQK + 8 * FRAG;        // f32  [8 v-tile][4 tok-tile][64][4] : U~
-constexpr int OFF_GAML = OFF_UT + 32 * FRAG;      // f32  [128] : exp(G_L)
-constexpr int REC_BYTES = OFF_GAML + 512;         // 90624 bytes per chunk and head
+constexpr int OFF_UT = OFF_AQK + 8 * FRAG;        // f16  [8 v-tile][4 tok-tile][64][4] : U~ * scale
+constexpr int OFF_USC = OFF_UT + 16 * FRAG;       // f32  [8 v-tile][4 tok-tile][16]    : 1 / scale
+constexpr int OFF_GAML = OFF_USC + 2048;          // f32  [128] : exp(G_L)
+constexpr int REC_BYTES = OFF_GAML + 512;         // 76288 bytes per chunk and head
 
 // ---- small helpers ---------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }

@@ -71,7 +71,7 @@ enum kda_state_dtype {
  *   B, T, H: as for kda_fwd;  N: number of sequences when cu_seqlens is used,
  *   0 otherwise. Returns 0 for invalid sizes (B < 1, T < 0, H < 1, N < 0).
  * The workspace holds the per-chunk intermediates of the chunked (WY) form
- * (about 88.5 KiB per 64-token chunk and head) and the varlen chunk tables.
+ * (74.5 KiB per 64-token chunk and head) and the varlen chunk tables.
  */
 size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N);
 

@@ -46,7 +46,7 @@ def test_version_and_status_strings():
 
 
 def test_workspace_size():
-    rec = 90624                         # bytes per (64-token chunk, head)
+    rec = 76288                         # bytes per (64-token chunk, head)
     al = lambda x: (x + 255) // 256 * 256
     assert kda.workspace_size(1, 8192, 64) == al(128 * 64 * rec)
     assert kda.workspace_size(4, 32768, 64) == al(4 * 512 * 64 * rec)
