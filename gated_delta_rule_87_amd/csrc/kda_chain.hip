@@ -194,8 +194,7 @@ __global__ __launch_bounds__(NW * 64) void kda_chain_kernel(FwdParams p, int nvg
 #pragma unroll
       for (int t = 0; t < VT; ++t) {
         const u32x2 uh = R.ut[w][t][mt][l];
-        const f32x2 u01 = __builtin_convertvector(__builtin_bit_cast(f16x2, uh.x), f32x2);
-        const f32x2 u23 = __builtin_convertvector(__builtin_bit_cast(f16x2, uh.y), f32x2);
+        const f32x2 u01 = unpack_f16x2(uh.x), u23 = unpack_f16x2(uh.y);
         U[t][mt] = f32x4{u01.x, u01.y, u23.x, u23.y} * R.usc[w][t][mt][lt] + acc[t] * iS[t];
       }
     }

@@ -63,6 +63,12 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
 }
 __device__ __forceinline__ uint16_t to_f16(float a) { return __builtin_bit_cast(uint16_t, (_Float16)a); }
+// packed fp16 pair -> two fp32. The argument is a plain scalar on purpose: clang
+// bit-casts an ext-vector element (v.y) from the vector's base address, so
+// callers must never pass such an element straight to __builtin_bit_cast.
+__device__ __forceinline__ f32x2 unpack_f16x2(uint32_t u) {
+  return __builtin_convertvector(__builtin_bit_cast(f16x2, u), f32x2);
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 u) { return __builtin_bit_cast(f16x8, u); }

@@ -1,0 +1,40 @@
+"""Static checks on the HIP sources (CPU only).
+
+clang lowers ``__builtin_bit_cast(T, v.y)`` on an ext_vector_type element by
+reading from the vector's base address, i.e. it returns the bits of ``v.x``.
+Kernels therefore only pass plain scalars or whole vectors to it (helpers such
+as ``unpack_f16x2`` take the element by value). This test keeps that rule.
+"""
+import glob
+import os
+import re
+
+CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gated_delta_rule_87_amd", "csrc")
+
+# __builtin_bit_cast(type, <expr ending in .x/.y/.z/.w or [i] of a vector>)
+_ELEMENT_ARG = re.compile(r"__builtin_bit_cast\s*\([^,()]+,\s*[A-Za-z_][\w\[\]\.]*\.(?:[xyzw]|s[0-9a-f])\s*\)")
+
+
+def _sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h")))
+
+
+def test_sources_exist():
+    names = {os.path.basename(p) for p in _sources()}
+    assert {"kda_device.h", "kda_intra.hip", "kda_chain.hip", "kda_sched.hip", "kda_recurrent.hip"} <= names
+
+
+def test_no_bit_cast_of_vector_element():
+    bad = []
+    for path in _sources():
+        for n, line in enumerate(open(path), 1):
+            if _ELEMENT_ARG.search(line):
+                bad.append(f"{os.path.basename(path)}:{n}: {line.strip()}")
+    assert not bad, "bit_cast of a vector element (miscompiled by clang):\n" + "\n".join(bad)
+
+
+def test_pattern_catches_the_bad_form():
+    assert _ELEMENT_ARG.search("f32x2 a = conv(__builtin_bit_cast(f16x2, uh.y), f32x2);")
+    assert _ELEMENT_ARG.search("__builtin_bit_cast(f16x2, R.ut[w][t].x)")
+    assert not _ELEMENT_ARG.search("__builtin_bit_cast(f16x2, u)")
+    assert not _ELEMENT_ARG.search("__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2))")
