@@ -2,6 +2,7 @@
 """Throughput of the chunked KDA forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1] [--no-cpu]
+    python bench.py --copy-calibration      # plain 1 GiB device copy, for HBM counter scaling
 
 A step is one kda_fwd call (the whole hot path: varlen scheduler when
 cu_seqlens is given, intra-chunk kernel, state-chain/output kernel) over one
@@ -10,13 +11,23 @@ fixed-length prefill B=1, T=8192, H=64, K=V=128 (bf16 inputs, stateless,
 fp32 final state). Prints ONE JSON line.
 
   value       tokens/s = tokens per step / mean step time (HIP events)
-  roofline    whole-call HBM roofline: algorithmic bytes per call / mean call
-              duration against 8 TB/s; algorithmic bytes = 1,282 B per
-              token-head (q, k, v, g, beta, out) + 64 KiB per fp32 state read
-              or written per (sequence, head); "traffic" is the measured HBM
-              bytes per call from rocprofv3 FETCH_SIZE/WRITE_SIZE (recorded in
-              profiles/traffic.json for a given kernel-source hash; null when the
-              kernels changed since)
+  roofline    HBM roofline of the dominant kernel (longest average launch):
+              its algorithmic bytes per launch / its average launch duration
+              (HIP events recorded by libkda on the launch stream around each
+              kernel, over the timed steps) against 8 TB/s. Algorithmic bytes
+              are the kernel's share of the path's 1,282 B per token-head: the
+              intra kernel reads q, k, v, g, beta (1,026 B), the chain kernel
+              writes out (256 B) and reads/writes the states (64 KiB fp32 or
+              32 KiB bf16 per sequence-head). "traffic" is the measured HBM
+              bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a
+              plain-copy calibration) recorded in profiles/traffic.json for the
+              current kernel-source hash, else null.
+  path        the same for the whole call: 1,282 B per token-head + state bytes
+              over the call's duration, and the bf16 MFMA fraction at
+              180,224 FLOP per token-head
+  kernels     per-kernel average duration, algorithmic bytes and the bytes the
+              design moves (including the per-chunk records written by the
+              intra kernel and read back by the chain kernel)
   cpu_baseline the fp64 CPU oracle timed on the host cores over the same
               workload (bounded: see "sample")
 """
@@ -36,6 +47,10 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FLOP_PER_TOKEN_HEAD = 180224          # dense C=64 chunk form, 2C(3K+2V) + 6KV
 BYTES_PER_TOKEN_HEAD = 1282           # q, k, v, g (4 x 256) + beta 2 + out 256
+IN_BYTES_PER_TOKEN_HEAD = 1026        # read by the intra kernel: q, k, v, g, beta
+OUT_BYTES_PER_TOKEN_HEAD = 256        # written by the chain kernel: out
+REC_BYTES = 76288                     # per-chunk record (64 tokens, one head) written by intra, read by chain
+CHUNK = 64
 
 
 def kernel_source_hash():
@@ -47,16 +62,39 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload_name):
+def recorded_traffic(workload_name, kernel):
+    """Measured HBM bytes per launch of `kernel`, if recorded for the current kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    ent = rec.get(workload_name)
+    ent = rec.get("workloads", {}).get(workload_name)
     if not ent or ent.get("source_hash") != kernel_source_hash():
         return None
-    return ent.get("bytes_per_call")
+    k = ent.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(steps):
+    """Plain device-to-device copy of 1 GiB: the counter-scaling reference."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    print(json.dumps({"copy_calibration": True, "bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                      "launches": steps + 1, "ms_per_launch": ms, "GBps_read_plus_write": 2 * n / ms / 1e6}),
+          flush=True)
 
 
 def cpu_threads():
@@ -77,11 +115,16 @@ def main():
     ap.add_argument("--workload", type=int, default=1, help="workload index (kda_inputs.workload)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--path", choices=["chunked", "recurrent"], default="chunked")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain 1 GiB device copy instead (HBM counter scaling reference)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {args.gpus}); "
-              "multi-GPU sharding is design-only here", file=sys.stderr)
+        print(f"bench.py: this implementation runs on exactly one GPU (asked for --gpus {args.gpus}); "
+              "sharding over several GPUs is a design, not built", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
 
     import torch
     import kda_inputs
@@ -122,6 +165,8 @@ def main():
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
+    if args.path == "chunked":
+        kda.profile_start(args.steps)
     t_wall = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
@@ -129,21 +174,37 @@ def main():
         ends[i].record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
+    per_kernel = kda.profile_stop() if args.path == "chunked" else {}
     per_call_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     span_ms = starts[0].elapsed_time(ends[-1])
     ms_per_step = span_ms / args.steps
     call_ms = sum(per_call_ms) / len(per_call_ms)
 
-    state_bytes = 0
-    sbytes = 4 if (w.state == 'fp32' or w.final == 'fp32') else 2
+    state_in = state_out = 0
     if w.state is not None:
-        state_bytes += nseq * H * 128 * 128 * sbytes
+        state_in = nseq * H * 128 * 128 * (4 if w.state == 'fp32' else 2)
     if w.final is not None:
-        state_bytes += nseq * H * 128 * 128 * (4 if w.final == 'fp32' else 2)
-    alg_bytes = BYTES_PER_TOKEN_HEAD * tokens * H + state_bytes
+        state_out = nseq * H * 128 * 128 * (4 if w.final == 'fp32' else 2)
+    alg_bytes = BYTES_PER_TOKEN_HEAD * tokens * H + state_in + state_out
     flops = FLOP_PER_TOKEN_HEAD * tokens * H
     achieved = alg_bytes / (call_ms * 1e-3) / 1e9
-    traffic = recorded_traffic(w.name)
+    if N:
+        lens = [int(a) for a in w.lengths]
+        chunks = sum((n + CHUNK - 1) // CHUNK for n in lens)
+    else:
+        chunks = B * ((T + CHUNK - 1) // CHUNK)
+    rec_bytes = chunks * H * REC_BYTES
+    alg = {"kda_sched_kernel": (0, 0),
+           "kda_intra_kernel": (IN_BYTES_PER_TOKEN_HEAD * tokens * H, rec_bytes),
+           "kda_chain_kernel": (OUT_BYTES_PER_TOKEN_HEAD * tokens * H + state_in + state_out, rec_bytes)}
+    kernels = {}
+    for name, (tot_ms, launches) in per_kernel.items():
+        if launches == 0:
+            continue
+        ms = tot_ms / launches
+        a, r = alg[name]
+        kernels[name] = {"avg_ms": ms, "launches": launches, "alg_bytes": a, "alg_GBps": a / (ms * 1e-3) / 1e9,
+                         "design_bytes": a + r, "design_GBps": (a + r) / (ms * 1e-3) / 1e9}
     res = {
         "metric": METRIC,
         "value": tokens / (ms_per_step * 1e-3),
@@ -160,21 +221,23 @@ def main():
         "config": {"workload": w.name, "B": B, "T": T, "H": H, "K": 128, "V": 128,
                    "varlen_seqs": N or None, "initial_state": w.state, "final_state": w.final,
                    "lower_bound": w.lower_bound, "path": args.path},
-        "roofline": {
-            "kernel": "kda_fwd (all kernels of one call)",
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
-            "traffic": traffic,
-            "alg_bytes_per_call": alg_bytes,
-            "call_ms": call_ms,
-            "mfma_tflops": flops / (call_ms * 1e-3) / 1e12,
-            "mfma_frac": flops / (call_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-        },
-        "wall_s_timed": t_wall,
     }
+    if kernels:
+        dom = max(kernels, key=lambda k: kernels[k]["avg_ms"])
+        kd = kernels[dom]
+        res["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": kd["alg_GBps"], "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": kd["alg_GBps"] / HBM_PEAK_GBS,
+                           "traffic": recorded_traffic(w.name, dom),
+                           "alg_bytes_per_launch": kd["alg_bytes"], "avg_launch_ms": kd["avg_ms"]}
+    else:
+        res["roofline"] = {"kernel": "kda_recurrent_kernel (whole call)", "bound": "hbm", "achieved": achieved,
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                           "alg_bytes_per_launch": alg_bytes, "avg_launch_ms": call_ms}
+    res["path"] = {"achieved_GBps": achieved, "frac_hbm": achieved / HBM_PEAK_GBS, "alg_bytes_per_call": alg_bytes,
+                   "call_ms": call_ms, "mfma_tflops": flops / (call_ms * 1e-3) / 1e12,
+                   "frac_mfma_bf16": flops / (call_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+    res["kernels"] = kernels
+    res["wall_s_timed"] = t_wall
 
     if not args.no_cpu:
         import numpy as np

@@ -24,7 +24,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["fwd", "fwd_recurrent", "workspace_size", "lib", "KDAError", "status_string", "LIB_PATH"]
+__all__ = ["fwd", "fwd_recurrent", "workspace_size", "lib", "KDAError", "status_string", "LIB_PATH",
+           "profile_start", "profile_stop"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
@@ -57,6 +58,14 @@ def _setup(L):
     L.kda_status_string.argtypes = [I]
     L.kda_version.restype = ctypes.c_char_p
     L.kda_version.argtypes = []
+    L.kda_profile_start.restype = I
+    L.kda_profile_start.argtypes = [I]
+    L.kda_profile_stop.restype = I
+    L.kda_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I), I]
+    L.kda_profile_kernel_count.restype = I
+    L.kda_profile_kernel_count.argtypes = []
+    L.kda_profile_kernel_name.restype = ctypes.c_char_p
+    L.kda_profile_kernel_name.argtypes = [I]
     return L
 
 
@@ -175,3 +184,22 @@ def fwd_recurrent(q, k, v, g, beta, scale: float, out, A_log, dt_bias, lower_bou
     if rc != 0:
         raise KDAError(rc, status_string(rc))
     return None
+
+
+def profile_start(max_calls: int) -> None:
+    """Time each kernel of the next ``max_calls`` fwd calls with HIP events on their stream."""
+    rc = lib().kda_profile_start(int(max_calls))
+    if rc != 0:
+        raise KDAError(rc, status_string(rc))
+
+
+def profile_stop() -> dict:
+    """Wait for the timed calls; return {kernel name: (summed ms, launches)} and stop timing."""
+    L = lib()
+    n = L.kda_profile_kernel_count()
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int * n)()
+    rc = L.kda_profile_stop(ms, cnt, n)
+    if rc != 0:
+        raise KDAError(rc, status_string(rc))
+    return {L.kda_profile_kernel_name(i).decode(): (ms[i], cnt[i]) for i in range(n)}

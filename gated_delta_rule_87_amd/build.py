@@ -21,6 +21,8 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
+    # MFMA results stay in VGPRs: no v_accvgpr_read before the VALU uses them
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

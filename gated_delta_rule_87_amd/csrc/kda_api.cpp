@@ -12,6 +12,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <vector>
 
 #include "../../include/kda.h"
@@ -123,6 +124,53 @@ kda::FwdParams make_params(const void* q, const void* k, const void* v, const vo
   return p;
 }
 
+
+// ---- optional per-kernel timing of kda_fwd ---------------------------------
+// While enabled, each kda_fwd call takes the next slot of NK + 1 HIP events and
+// records one on the call's stream before its first kernel and one after each
+// kernel, so consecutive events bracket one kernel each.
+constexpr int NK = 3;   // 0 varlen scheduler, 1 intra-chunk, 2 state chain + output
+const char* const kKernelNames[NK] = {"kda_sched_kernel", "kda_intra_kernel", "kda_chain_kernel"};
+
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  int cap = 0, used = 0;
+  std::vector<hipEvent_t> ev;   // cap x (NK + 1)
+  std::vector<uint8_t> ran;     // cap x NK: kernel i launched in that call
+};
+Profiler& profiler() {
+  static Profiler P;
+  return P;
+}
+void profiler_release(Profiler& P) {
+  for (hipEvent_t e : P.ev) (void)hipEventDestroy(e);
+  P.ev.clear();
+  P.ran.clear();
+  P.on = false;
+  P.cap = P.used = 0;
+}
+
+// Takes a slot for one call (or none when timing is off or the slots are used up).
+struct CallTimer {
+  hipEvent_t* ev = nullptr;
+  uint8_t* ran = nullptr;
+  hipStream_t st;
+  explicit CallTimer(hipStream_t s) : st(s) {
+    Profiler& P = profiler();
+    std::lock_guard<std::mutex> lk(P.mu);
+    if (!P.on || P.used >= P.cap) return;
+    ev = &P.ev[(size_t)P.used * (NK + 1)];
+    ran = &P.ran[(size_t)P.used * NK];
+    ++P.used;
+  }
+  hipError_t mark(int i) {   // i = 0: before the first kernel; i > 0: after kernel i - 1
+    return ev ? hipEventRecord(ev[i], st) : hipSuccess;
+  }
+  void launched(int k) {
+    if (ran) ran[k] = 1;
+  }
+};
 }  // namespace
 
 extern "C" {
@@ -171,13 +219,25 @@ int kda_fwd(const void* q, const void* k, const void* v, const void* g, const vo
                  (long long)B, (long long)T, (long long)H, (long long)N, (long long)L.max_chunks, L.total,
                  (int)varlen);
 
-  hipError_t e = hipSuccess;
-  if (varlen && L.max_chunks > 0)
+  CallTimer tm(st);
+  hipError_t e = tm.mark(0);
+  if (e == hipSuccess && varlen && L.max_chunks > 0) {
     e = kda::launch_sched(cu_seqlens, (int32_t)N, (int32_t)T, (int32_t)L.max_chunks,
                           reinterpret_cast<int2*>(ws + L.seq_tab), reinterpret_cast<int2*>(ws + L.chunk_tab),
                           reinterpret_cast<int2*>(ws + L.seq_span), st);
-  if (e == hipSuccess) e = kda::launch_intra(p, st);
-  if (e == hipSuccess) e = kda::launch_chain(p, st);
+    tm.launched(0);
+  }
+  if (e == hipSuccess) e = tm.mark(1);
+  if (e == hipSuccess) {
+    e = kda::launch_intra(p, st);
+    tm.launched(1);
+  }
+  if (e == hipSuccess) e = tm.mark(2);
+  if (e == hipSuccess) {
+    e = kda::launch_chain(p, st);
+    tm.launched(2);
+  }
+  if (e == hipSuccess) e = tm.mark(3);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -218,5 +278,62 @@ const char* kda_status_string(int status) {
 }
 
 const char* kda_version(void) { return "0.1.0 gfx950"; }
+
+int kda_profile_start(int max_calls) {
+  if (max_calls < 1 || max_calls > 65536) return KDA_ERR_VALUE;
+  Profiler& P = profiler();
+  std::lock_guard<std::mutex> lk(P.mu);
+  profiler_release(P);
+  P.ev.reserve((size_t)max_calls * (NK + 1));
+  for (size_t i = 0; i < (size_t)max_calls * (NK + 1); ++i) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) {
+      profiler_release(P);
+      return KDA_ERR_HIP;
+    }
+    P.ev.push_back(e);
+  }
+  P.ran.assign((size_t)max_calls * NK, 0);
+  P.cap = max_calls;
+  P.used = 0;
+  P.on = true;
+  return KDA_OK;
+}
+
+int kda_profile_stop(double* total_ms, int* launches, int n_kernels) {
+  if (!total_ms || !launches) return KDA_ERR_NULL;
+  if (n_kernels < NK) return KDA_ERR_SHAPE;
+  Profiler& P = profiler();
+  std::lock_guard<std::mutex> lk(P.mu);
+  if (!P.on) return KDA_ERR_VALUE;
+  for (int i = 0; i < n_kernels; ++i) {
+    total_ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  int rc = KDA_OK;
+  for (int c = 0; c < P.used && rc == KDA_OK; ++c) {
+    hipEvent_t* ev = &P.ev[(size_t)c * (NK + 1)];
+    if (hipEventSynchronize(ev[NK]) != hipSuccess) {
+      rc = KDA_ERR_HIP;
+      break;
+    }
+    for (int k = 0; k < NK; ++k) {
+      if (!P.ran[(size_t)c * NK + k]) continue;
+      float ms = 0.0f;
+      if (hipEventElapsedTime(&ms, ev[k], ev[k + 1]) != hipSuccess) {
+        rc = KDA_ERR_HIP;
+        break;
+      }
+      total_ms[k] += ms;
+      launches[k] += 1;
+    }
+  }
+  profiler_release(P);
+  return rc;
+}
+
+int kda_profile_kernel_count(void) { return NK; }
+
+const char* kda_profile_kernel_name(int i) { return (i >= 0 && i < NK) ? kKernelNames[i] : ""; }
 
 }  // extern "C"

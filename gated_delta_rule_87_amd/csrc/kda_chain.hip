@@ -43,6 +43,9 @@ constexpr int NSHARED = 56;   // fragments per chunk shared by all value tiles
 
 #define LDSPTR(p) ((__attribute__((address_space(3))) void*)(p))
 
+// buffer resource word 3 for raw (stride 0) dword-granular loads on gfx9-family parts
+constexpr int RSRC_WORD3 = 0x00020000;
+
 // s_waitcnt vmcnt(n) with expcnt/lgkmcnt left unconstrained (gfx9 encoding)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -56,6 +59,14 @@ __device__ __forceinline__ float row_absmax(const f32x4* x, int n) {
   float m = 0.0f;
   for (int i = 0; i < n; ++i) m = fmaxf(m, fmaxf(fmaxf(fabsf(x[i].x), fabsf(x[i].y)), fmaxf(fabsf(x[i].z), fabsf(x[i].w))));
   return max_over_groups(m);
+}
+
+// the same pointer in every lane, made explicit so it lives in SGPRs
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
 }
 
 __device__ __forceinline__ u32x4 pack_pair_f16(f32x4 a, f32x4 b, float s) {
@@ -128,26 +139,31 @@ __global__ __launch_bounds__(NW * 64) void kda_chain_kernel(FwdParams p, int nvg
   }
   wait_vmcnt<0>();   // the loop below then carries no pending register loads
 
-  // one prefetch = NSHARED/NW shared fragments + 4*VT U~ fragments + Gamma_L, all straight into LDS
+  const int lane16 = l * 16;   // this lane's 16 bytes of a 1 KiB fragment (VGPR offset of every load)
+  // one prefetch = NSHARED/NW shared fragments + 2*VT U~ halves + VT scale rows + Gamma_L, all
+  // straight into LDS with buffer loads: a scalar resource per record, the lane offset in one
+  // VGPR and the in-record offset in an SGPR, so no per-load vector address arithmetic. The
+  // resource spans exactly one record, which the hardware range-checks.
   auto prefetch = [&](int j, int buf) {
-    const uint8_t* rec = p.rec + ((size_t)(c0 + j) * H + h) * REC_BYTES;
+    const uint8_t* rec = uniform_ptr(p.rec + ((size_t)(c0 + j) * H + h) * REC_BYTES);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, REC_BYTES, RSRC_WORD3);
 #pragma unroll
     for (int i = 0; i < NSHARED / NW; ++i) {
       const int f = i * NW + w;
-      __builtin_amdgcn_global_load_lds(rec + f * FRAG + l * 16, LDSPTR(&ring[buf].shared[f][0]), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDSPTR(&ring[buf].shared[f][0]), 16, lane16, f * FRAG, 0, 0);
     }
 #pragma unroll
     for (int t = 0; t < VT; ++t) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
-        __builtin_amdgcn_global_load_lds(rec + OFF_UT + (vt0 + t) * 2048 + hh * FRAG + l * 16,
-                                         LDSPTR(&ring[buf].ut[w][t][2 * hh][0]), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDSPTR(&ring[buf].ut[w][t][2 * hh][0]), 16, lane16,
+                                                 OFF_UT + (vt0 + t) * 2048 + hh * FRAG, 0, 0);
       if (l < 16)
-        __builtin_amdgcn_global_load_lds(rec + OFF_USC + (vt0 + t) * 256 + l * 16,
-                                         LDSPTR(&ring[buf].usc[w][t][0][0]), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDSPTR(&ring[buf].usc[w][t][0][0]), 16, lane16,
+                                                 OFF_USC + (vt0 + t) * 256, 0, 0);
     }
     if (l < 32)
-      __builtin_amdgcn_global_load_lds(rec + OFF_GAML + l * 16, LDSPTR(&ring[buf].gam[w][0]), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDSPTR(&ring[buf].gam[w][0]), 16, lane16, OFF_GAML, 0, 0);
   };
   constexpr int KPF = NSHARED / NW + 3 * VT + 1;   // vector-memory ops issued per prefetch
 

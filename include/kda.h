@@ -134,6 +134,31 @@ const char *kda_status_string(int status);
 /* kda_version -- library version string, e.g. "0.1.0 gfx950". */
 const char *kda_version(void);
 
+/*
+ * Per-kernel timing of kda_fwd (a measurement hook; results are unchanged).
+ *
+ * kda_profile_start(max_calls): from now on, each of the next max_calls
+ *   kda_fwd calls records HIP events on its stream before its first kernel and
+ *   after each kernel (the events are created here, not per call). Calls
+ *   beyond max_calls are not timed. Starting again discards earlier recordings.
+ *   Returns KDA_ERR_VALUE unless 1 <= max_calls <= 65536, KDA_ERR_HIP if an
+ *   event cannot be created.
+ * kda_profile_stop(total_ms, launches, n_kernels): waits for the recorded
+ *   events and writes, for each kernel i < kda_profile_kernel_count(), the
+ *   summed milliseconds over the timed calls into total_ms[i] and the number
+ *   of timed calls that launched it into launches[i] (host arrays of
+ *   n_kernels >= the kernel count); then stops timing and frees the events.
+ *   Returns KDA_ERR_NULL, KDA_ERR_SHAPE (n_kernels too small), KDA_ERR_VALUE
+ *   (timing not started) or KDA_ERR_HIP.
+ * kda_profile_kernel_name(i): static name of kernel i ("" when out of range).
+ * One interval runs from one event to the next on the same stream: the
+ * kernel's execution plus its launch gap.
+ */
+int kda_profile_start(int max_calls);
+int kda_profile_stop(double *total_ms, int *launches, int n_kernels);
+int kda_profile_kernel_count(void);
+const char *kda_profile_kernel_name(int i);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,8 @@ def declared_functions():
 def test_header_symbols_exported():
     names = declared_functions()
     assert {"kda_fwd", "kda_fwd_recurrent", "kda_fwd_workspace_size", "kda_status_string",
-            "kda_version"} <= set(names)
+            "kda_version", "kda_profile_start", "kda_profile_stop", "kda_profile_kernel_count",
+            "kda_profile_kernel_name"} <= set(names)
     L = ctypes.CDLL(kda.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"libkda.so does not export {n}"
@@ -135,3 +136,20 @@ def test_api_table_fixture_matches_binding():
     assert table["A_log"] == ("fp32", "[H]") and table["dt_bias"] == ("fp32", "[H, K]")
     assert table["cu_seqlens"] == ("int64", "[N+1]")
     assert table["initial_state"][0] == "bf16/fp32/None"
+
+
+def test_profile_hook_host_paths():
+    """Timing-hook argument checks that make no HIP call (no start with a valid count)."""
+    L = kda.lib()
+    n = L.kda_profile_kernel_count()
+    assert n == 3
+    assert [L.kda_profile_kernel_name(i) for i in range(n)] == [b"kda_sched_kernel", b"kda_intra_kernel",
+                                                                   b"kda_chain_kernel"]
+    assert L.kda_profile_kernel_name(-1) == b"" and L.kda_profile_kernel_name(n) == b""
+    assert L.kda_profile_start(0) == EVALUE
+    assert L.kda_profile_start(65537) == EVALUE
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int * n)()
+    assert L.kda_profile_stop(None, cnt, n) == ENULL
+    assert L.kda_profile_stop(ms, cnt, n - 1) == ESHAPE
+    assert L.kda_profile_stop(ms, cnt, n) == EVALUE      # timing was never started
