@@ -38,3 +38,38 @@ def test_pattern_catches_the_bad_form():
     assert _ELEMENT_ARG.search("__builtin_bit_cast(f16x2, R.ut[w][t].x)")
     assert not _ELEMENT_ARG.search("__builtin_bit_cast(f16x2, u)")
     assert not _ELEMENT_ARG.search("__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2))")
+
+
+def _device_asm(source, tmp_path):
+    import subprocess
+    from gated_delta_rule_87_amd.build import FLAGS, HIPCC
+    if not os.access(HIPCC, os.X_OK):
+        import pytest
+        pytest.skip("hipcc not available")
+    out = tmp_path / "k.s"
+    flags = [f for f in FLAGS if f not in ("-shared", "-fPIC")]
+    r = subprocess.run([HIPCC, *flags, "--cuda-device-only", "-S", "-o", str(out), os.path.join(CSRC, source)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return out.read_text().splitlines()
+
+
+def test_chain_lds_dma_has_uniform_destination(tmp_path):
+    """Every LDS DMA load of the chain kernel takes M0 (its LDS destination, one per
+    wave) from scalar arithmetic, never from a per-lane value via v_readfirstlane, and
+    no load sits in a waterfall loop. A lane-dependent branch around such a load once
+    let the optimiser merge call sites and route lanes to the wrong LDS address."""
+    lines = [ln.strip() for ln in _device_asm("kda_chain.hip", tmp_path)]
+    loads = [i for i, ln in enumerate(lines) if ln.startswith("buffer_load_dwordx4") and ln.endswith("lds")]
+    assert len(loads) >= 2 * 56
+    rfl = {}
+    for i, ln in enumerate(lines):
+        m = re.match(r"v_readfirstlane_b32 (s\d+),", ln)
+        if m:
+            rfl[m.group(1)] = i
+        m = re.match(r"s_mov_b32 m0, (s\d+)$", ln)
+        if m and m.group(1) in rfl and i - rfl[m.group(1)] < 8:
+            raise AssertionError(f"M0 set from v_readfirstlane at asm line {i}: {ln}")
+    for i, ln in enumerate(lines):
+        if ln.startswith("s_xor_b64 exec, exec"):
+            raise AssertionError(f"waterfall loop (s_xor_b64 exec) at asm line {i}")
