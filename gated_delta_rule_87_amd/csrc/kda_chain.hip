@@ -20,13 +20,12 @@
 //                           column scaled by a power of two) in LDS
 //   output wave NW + s      computes O^T of value tile s from those operands and
 //                           the chunk's Q^.Gamma and Aqk, stores out
-//   DMA wave 2 NW           streams chunk j + 1's record into the other half of
-//                           a two-deep LDS ring with buffer loads while chunk j
-//                           is computed
-// Two workgroup barriers per chunk: (A) chunk j's record and S0's operands are
-// in LDS; (B) U's operands are in LDS. The state update runs while the output
-// waves finish O, so neither the loads nor the output sit on the state
-// recurrence's critical path.
+//   DMA wave 2 NW           streams the records into LDS with buffer loads, 1.5
+//                           chunk steps ahead of their use
+// Two workgroup barriers per chunk: (A) the first part of chunk j's record and
+// S0's operands are in LDS; (B) the second part and U's operands are in LDS.
+// The state update runs while the output waves finish O, so neither the loads
+// nor the output sit on the state recurrence's critical path.
 //
 // Precision: MFMA operands are fp16. Each state row and each column of U is
 // scaled by its own power of two (max |x| * s in [1, 2)) before rounding, so
@@ -38,8 +37,6 @@
 namespace kda {
 namespace {
 
-constexpr int NSHARED = 56;   // fragments per chunk shared by all value tiles
-
 #define LDSPTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 // buffer resource word 3 for raw (stride 0) dword-granular loads on gfx9-family parts
@@ -48,8 +45,14 @@ constexpr int RSRC_WORD3 = 0x00020000;
 // This wave's LDS accesses are complete, then the workgroup barrier. The asm
 // is also a compiler memory barrier, so no LDS access moves across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// All of this wave's vector-memory operations (the LDS DMA included) are done.
-__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// At most N of this wave's vector-memory operations (the LDS DMA included) are
+// still outstanding; they complete in issue order. The counter holds at most 63.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  constexpr int n = N > 63 ? 63 : N;
+  __builtin_amdgcn_s_waitcnt((n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+  asm volatile("" ::: "memory");
+}
 
 // the same pointer in every lane, made explicit so it lives in SGPRs
 __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
@@ -83,13 +86,26 @@ constexpr int USC_WIN = 1024;
 constexpr int GAM_WIN_OFF = OFF_GAML - 512;
 static_assert(OFF_USC + 2048 == OFF_GAML && OFF_GAML + 512 == REC_BYTES, "record tail layout");
 
+// A chunk's record is staged in two parts, each in its own two-slot ring: the
+// part read between barriers (A) and (B) of a chunk step, and the part read
+// between (B) and the next (A). A slot is refilled as soon as its part of the
+// step is over, so every load is issued 1.5 chunk steps before it is needed.
 template <int NW>
-struct ChainRing {               // one chunk's record, as the waves read it
-  u32x4 shared[NSHARED][64];     // -W, Qg, K'^T, Aqk fragments (all value tiles)
+struct ChainPart1 {              // read in [A, B): U and the S0 half of O
+  u32x4 wneg[16][64];            // -W fragments [token tile * 4 + k-step][lane]
+  u32x4 qg[16][64];              // Q^.Gamma fragments [token tile * 4 + k-step][lane]
   u32x2 ut[NW][4][64];           // U~ (fp16, scaled) of each value tile [token tile][lane]
   float usc[USC_WIN / 4];        // [s][token tile][value column]: 1 / scale (first NW*64 floats)
+};
+template <int NW>
+struct ChainPart2 {              // read in [B, next A): the state update and the U half of O
+  u32x4 kp[16][64];              // K'^T fragments [channel tile * 2 + k-step][lane]
+  u32x4 aqk[6][64];              // the Aqk fragments that are not all zero (see AQK_FRAG)
   float gamw[256];               // Gamma_L in [128, 256)
 };
+// Aqk fragment (token tile nt, k-step q) with q <= nt / 2 -> slot in ChainPart2::aqk
+__device__ __forceinline__ constexpr int aqk_slot(int nt, int q) { return nt < 2 ? nt : 2 * nt - 2 + q; }
+constexpr int AQK_FRAG[6] = {0, 2, 4, 5, 6, 7};   // record fragment index (nt * 2 + q) of each slot
 
 template <int NW>
 struct ChainXchg {               // state wave -> output wave operands of one chunk
@@ -101,7 +117,8 @@ struct ChainXchg {               // state wave -> output wave operands of one ch
 
 template <int NW>
 __global__ __launch_bounds__((2 * NW + 1) * 64) void kda_chain_kernel(FwdParams p, int nvg) {
-  __shared__ ChainRing<NW> ring[2];
+  __shared__ ChainPart1<NW> r1[2];
+  __shared__ ChainPart2<NW> r2[2];
   __shared__ ChainXchg<NW> xc;
 
   const int H = p.H;
@@ -134,35 +151,70 @@ __global__ __launch_bounds__((2 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
 
   if (w == 2 * NW) {
     // ---------------- DMA wave ----------------
-    // one chunk = NSHARED shared fragments + per value tile two U~ halves + the scale
-    // and Gamma_L windows, straight into LDS with buffer loads: a scalar resource per
-    // record (which the hardware range-checks), the lane offset in one VGPR, the
-    // in-record offset in an SGPR
+    // Straight into LDS with buffer loads: a scalar resource per record (which the
+    // hardware range-checks), the lane offset in one VGPR, the in-record offset in an
+    // SGPR. Issue order P1(0) P2(0) P1(1) | P2(1) P1(2) | P2(2) P1(3) | ..., and loads
+    // complete in issue order, so each wait names how many later loads may still fly.
     const int lane16 = l * 16;
-    auto load_chunk = [&](int j, int buf) {
+    auto rsrc = [&](int j) {
       const uint8_t* rec = uniform_ptr(p.rec + ((size_t)(c0 + j) * H + h) * REC_BYTES);
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, REC_BYTES, RSRC_WORD3);
+      return __builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, REC_BYTES, RSRC_WORD3);
+    };
+    auto load_part1 = [&](int j) {
+      const __amdgpu_buffer_rsrc_t rs = rsrc(j);
+      ChainPart1<NW>& d = r1[j & 1];
 #pragma unroll
-      for (int f = 0; f < NSHARED; ++f)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDSPTR(&ring[buf].shared[f][0]), 16, lane16, f * FRAG, 0, 0);
+      for (int f = 0; f < 16; ++f)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDSPTR(&d.wneg[f][0]), 16, lane16, OFF_WNEG + f * FRAG, 0, 0);
+#pragma unroll
+      for (int f = 0; f < 16; ++f)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDSPTR(&d.qg[f][0]), 16, lane16, OFF_QG + f * FRAG, 0, 0);
 #pragma unroll
       for (int s = 0; s < NW; ++s) {
-        const int vt = vg * NW + s;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDSPTR(&ring[buf].ut[s][2 * hh][0]), 16, lane16,
-                                                   OFF_UT + vt * 2048 + hh * FRAG, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDSPTR(&d.ut[s][2 * hh][0]), 16, lane16,
+                                                   OFF_UT + (vg * NW + s) * 2048 + hh * FRAG, 0, 0);
       }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDSPTR(&ring[buf].usc[0]), 16, lane16, OFF_USC + NW * 256 * vg, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDSPTR(&ring[buf].gamw[0]), 16, lane16, GAM_WIN_OFF, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDSPTR(&d.usc[0]), 16, lane16, OFF_USC + NW * 256 * vg, 0, 0);
     };
-    if (nc > 0) load_chunk(0, 0);
-    wait_vm_all();
+    auto load_part2 = [&](int j) {
+      const __amdgpu_buffer_rsrc_t rs = rsrc(j);
+      ChainPart2<NW>& d = r2[j & 1];
+#pragma unroll
+      for (int f = 0; f < 16; ++f)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDSPTR(&d.kp[f][0]), 16, lane16, OFF_KP + f * FRAG, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 6; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDSPTR(&d.aqk[i][0]), 16, lane16, OFF_AQK + AQK_FRAG[i] * FRAG, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDSPTR(&d.gamw[0]), 16, lane16, GAM_WIN_OFF, 0, 0);
+    };
+    constexpr int N1 = 32 + 2 * NW + 1, N2 = 16 + 6 + 1;   // loads per part
+    if (nc > 0) {
+      load_part1(0);
+      load_part2(0);
+      if (nc > 1) {
+        load_part1(1);
+        wait_vmcnt<N2 + N1>();                     // P1(0) landed
+      } else {
+        wait_vmcnt<N2>();
+      }
+    }
     for (int j = 0; j < nc; ++j) {
-      lds_barrier();                               // (A): chunk j landed; ring[(j+1)&1] is free
-      if (j + 1 < nc) load_chunk(j + 1, (j + 1) & 1);
-      lds_barrier();                               // (B)
-      wait_vm_all();                               // chunk j+1 landed before the next (A)
+      lds_barrier();                               // (A): P1(j) landed; P2 slot (j+1)&1 is free
+      if (j + 1 < nc) {
+        load_part2(j + 1);
+        wait_vmcnt<N1 + N2>();                     // P2(j) landed (P1(j+1), P2(j+1) may fly)
+      } else {
+        wait_vmcnt<0>();
+      }
+      lds_barrier();                               // (B): P2(j) landed; P1 slot j&1 is free
+      if (j + 2 < nc) {
+        load_part1(j + 2);
+        wait_vmcnt<N2 + N1>();                     // P1(j+1) landed (P2(j+1), P1(j+2) may fly)
+      } else if (j + 1 < nc) {
+        wait_vmcnt<N2>();
+      }
     }
     return;
   }
@@ -208,7 +260,8 @@ __global__ __launch_bounds__((2 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
     publish_state();
 
     for (int j = 0; j < nc; ++j) {
-      const ChainRing<NW>& R = ring[j & 1];
+      const ChainPart1<NW>& P1 = r1[j & 1];
+      const ChainPart2<NW>& P2 = r2[j & 1];
       lds_barrier();   // (A)
 
       // U = U~ + (-W) S0^T     D layout: lane <-> v, registers <-> tokens 16 mt + 4 gq + j
@@ -217,10 +270,10 @@ __global__ __launch_bounds__((2 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
       for (int mt = 0; mt < 4; ++mt) {
         f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc = mfma_f16(R.shared[mt * 4 + q][l], sf[q], acc);
-        const u32x2 uh = R.ut[s][mt][l];
+        for (int q = 0; q < 4; ++q) acc = mfma_f16(P1.wneg[mt * 4 + q][l], sf[q], acc);
+        const u32x2 uh = P1.ut[s][mt][l];
         const f32x2 u01 = unpack_f16x2(uh.x), u23 = unpack_f16x2(uh.y);
-        U[mt] = f32x4{u01.x, u01.y, u23.x, u23.y} * R.usc[s * 64 + mt * 16 + lt] + acc * iS;
+        U[mt] = f32x4{u01.x, u01.y, u23.x, u23.y} * P1.usc[s * 64 + mt * 16 + lt] + acc * iS;
       }
       float sU, iU;
       pow2_scale(row_absmax(U, 4), sU, iU);
@@ -236,10 +289,10 @@ __global__ __launch_bounds__((2 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
       // S1^T = Diag(Gamma_L) S0^T + K'^T U
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
-        const f32x4 g4 = *reinterpret_cast<const f32x4*>(&R.gamw[128 + 16 * mt + 4 * gq]);
+        const f32x4 g4 = *reinterpret_cast<const f32x4*>(&P2.gamw[128 + 16 * mt + 4 * gq]);
         f32x4 acc = {0, 0, 0, 0};
-        acc = mfma_f16(R.shared[32 + mt * 2][l], uf[0], acc);
-        acc = mfma_f16(R.shared[32 + mt * 2 + 1][l], uf[1], acc);
+        acc = mfma_f16(P2.kp[mt * 2][l], uf[0], acc);
+        acc = mfma_f16(P2.kp[mt * 2 + 1][l], uf[1], acc);
         S[mt] = S[mt] * g4 + acc * iU;
       }
       // the output wave has read S0's operands before (B); publish S1's for the next chunk
@@ -265,7 +318,8 @@ __global__ __launch_bounds__((2 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
   // Register jj of lane group gq belongs to value row 4 gq + jj of the tile.
   const float scale = p.scale;
   for (int j = 0; j < nc; ++j) {
-    const ChainRing<NW>& R = ring[j & 1];
+    const ChainPart1<NW>& P1 = r1[j & 1];
+    const ChainPart2<NW>& P2 = r2[j & 1];
     lds_barrier();   // (A)
     u32x4 sf[4];
 #pragma unroll
@@ -276,7 +330,7 @@ __global__ __launch_bounds__((2 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
     for (int nt = 0; nt < 4; ++nt) {
       aq[nt] = f32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) aq[nt] = mfma_f16(sf[q], R.shared[16 + nt * 4 + q][l], aq[nt]);
+      for (int q = 0; q < 4; ++q) aq[nt] = mfma_f16(sf[q], P1.qg[nt * 4 + q][l], aq[nt]);
       aq[nt] *= oS;
     }
     lds_barrier();   // (B)
@@ -286,8 +340,8 @@ __global__ __launch_bounds__((2 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
     const int L = min(CH, len - j * CH);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      f32x4 aa = mfma_f16(uf0, R.shared[48 + nt * 2][l], f32x4{0, 0, 0, 0});
-      if (nt >= 2) aa = mfma_f16(uf1, R.shared[48 + nt * 2 + 1][l], aa);
+      f32x4 aa = mfma_f16(uf0, P2.aqk[aqk_slot(nt, 0)][l], f32x4{0, 0, 0, 0});
+      if (nt >= 2) aa = mfma_f16(uf1, P2.aqk[aqk_slot(nt, 1)][l], aa);
       const int tok = 16 * nt + lt;
       if (tok < L) {
         const f32x4 o = aq[nt] + aa * oU;
