@@ -138,7 +138,9 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
   const int H = p.H;
   const int slot = blockIdx.x;
   const int h = slot % H;
-  const int ci = slot / H;
+  // chunks are launched last-first: the records of a sequence's first chunks are then
+  // the most recently written, still in the last-level cache when the chain starts there
+  const int ci = p.map.max_chunks - 1 - slot / H;
 
   int t0, L;
   if (p.map.chunk_tab) {
