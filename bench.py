@@ -32,7 +32,6 @@ fp32 final state). Prints ONE JSON line.
               workload (bounded: see "sample")
 """
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -54,12 +53,8 @@ CHUNK = 64
 
 
 def kernel_source_hash():
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "gated_delta_rule_87_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
-    return h.hexdigest()[:16]
+    from gated_delta_rule_87_amd.rocprof_summary import kernel_source_hash as h
+    return h()
 
 
 def recorded_traffic(workload_name, kernel):
