@@ -42,9 +42,6 @@ namespace {
 // buffer resource word 3 for raw (stride 0) dword-granular loads on gfx9-family parts
 constexpr int RSRC_WORD3 = 0x00020000;
 
-// This wave's LDS accesses are complete, then the workgroup barrier. The asm
-// is also a compiler memory barrier, so no LDS access moves across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 // At most N of this wave's vector-memory operations (the LDS DMA included) are
 // still outstanding; they complete in issue order. The counter holds at most 63.
 template <int N>

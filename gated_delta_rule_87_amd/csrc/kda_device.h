@@ -70,6 +70,12 @@ __device__ __forceinline__ f32x2 unpack_f16x2(uint32_t u) {
   return __builtin_convertvector(__builtin_bit_cast(f16x2, u), f32x2);
 }
 
+// Workgroup barrier that orders LDS accesses only: this wave's LDS operations are
+// complete, then s_barrier. Unlike __syncthreads() it does not wait for global
+// loads or stores in flight (a release fence would add s_waitcnt vmcnt(0)). The
+// asm is also a compiler memory barrier, so no memory access moves across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 u) { return __builtin_bit_cast(f16x8, u); }
 

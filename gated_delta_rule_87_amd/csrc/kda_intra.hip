@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
       sm.beta[tok] = valid ? sigmoidf_fast(b) : 0.0f;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---------------- phase C: per-channel constants of the chunk -------------
   {
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
     sm.c2[wa + 2][c] = __expf(GL - rB1);
     if (tid < KD) reinterpret_cast<float*>(rec + OFF_GAML)[c] = __expf(GL);
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---------------- phase B: operands, diagonal grams, permuted copies -------
   const u32x4 idh0 = perm_operand(lt, gq, 0, 0x3C00u), idh1 = perm_operand(lt, gq, 1, 0x3C00u);
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
       *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(&sm.vt[ct][w >> 1][l]) + half) = pk4_bf16(dv);
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---------------- phase D: off-diagonal grams, A to LDS, Aqk out ----------
   {
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---------------- phase E: Tm = (I + A)^-1 (fp32) ----------------------------
   {
@@ -379,11 +379,11 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
       for (int i = 0; i < 16; ++i) sm.u.tm[tmi(16 * w + i, 16 * w + lt)] = x[i];
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (w == 0) solve_column_block<0>(sm, lt, gq);
   else if (w == 1) solve_column_block<1>(sm, lt, gq);
   else if (w == 2) solve_column_block<2>(sm, lt, gq);
-  __syncthreads();
+  lds_barrier();
 
   // ---------------- phase F: W = Tm diag(beta) K^.Gamma,  U~ = Tm diag(beta) V -
   {
