@@ -27,10 +27,10 @@ inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
   int64_t max_chunks = 0;
-  size_t rec = 0, seq_tab = 0, chunk_tab = 0, seq_span = 0, total = 0;
+  size_t rec = 0, seq_tab = 0, chunk_tab = 0, seq_span = 0, seq_order = 0, total = 0;
 };
 
-// Workspace regions: chunk records | seq_tab | chunk_tab | seq_span.
+// Workspace regions: chunk records | seq_tab | chunk_tab | seq_span | seq_order.
 bool make_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool varlen, Layout& L) {
   if (B < 1 || T < 0 || H < 1 || N < 0) return false;
   if (varlen) {
@@ -49,6 +49,8 @@ bool make_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool varlen, Layout
   off = align_up(off + (varlen ? (size_t)L.max_chunks * sizeof(int2) : 0));
   L.seq_span = off;
   off = align_up(off + (varlen ? (size_t)N * sizeof(int2) : 0));
+  L.seq_order = off;
+  off = align_up(off + (varlen ? (size_t)N * sizeof(int32_t) : 0));
   L.total = off;
   return true;
 }
@@ -213,6 +215,7 @@ int kda_fwd(const void* q, const void* k, const void* v, const void* g, const vo
     p.map.seq_tab = reinterpret_cast<const int2*>(ws + L.seq_tab);
     p.map.chunk_tab = reinterpret_cast<const int2*>(ws + L.chunk_tab);
     p.map.seq_span = reinterpret_cast<const int2*>(ws + L.seq_span);
+    p.map.seq_order = reinterpret_cast<const int32_t*>(ws + L.seq_order);
   }
   if (env_flag("KDA_LOG"))
     std::fprintf(stderr, "[kda] fwd B=%lld T=%lld H=%lld N=%lld chunks=%lld workspace=%zu varlen=%d\n",
@@ -224,7 +227,8 @@ int kda_fwd(const void* q, const void* k, const void* v, const void* g, const vo
   if (e == hipSuccess && varlen && L.max_chunks > 0) {
     e = kda::launch_sched(cu_seqlens, (int32_t)N, (int32_t)T, (int32_t)L.max_chunks,
                           reinterpret_cast<int2*>(ws + L.seq_tab), reinterpret_cast<int2*>(ws + L.chunk_tab),
-                          reinterpret_cast<int2*>(ws + L.seq_span), st);
+                          reinterpret_cast<int2*>(ws + L.seq_span), reinterpret_cast<int32_t*>(ws + L.seq_order),
+                          st);
     tm.launched(0);
   }
   if (e == hipSuccess) e = tm.mark(1);

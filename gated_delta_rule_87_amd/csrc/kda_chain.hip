@@ -126,7 +126,9 @@ __global__ __launch_bounds__((2 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
   const int vg = rest % nvg, grp = rest / nvg;
   const int nh = grp * 8 + xcd;
   if (nh >= NH) return;   // uniform over the block
-  const int n = nh / H, h = nh - n * H;
+  // varlen: walk the sequences longest first, so long chains do not start last
+  const int rank = nh / H, h = nh - rank * H;
+  const int n = p.map.seq_order ? __builtin_amdgcn_readfirstlane(p.map.seq_order[rank]) : rank;
 
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, uniform
   const int l = threadIdx.x & 63, lt = l & 15, gq = l >> 4;

@@ -13,6 +13,7 @@ struct ChunkMap {
   const int2* chunk_tab;   // varlen: [max_chunks] {t0, len}; len = 0 -> unused slot
   const int2* seq_tab;     // varlen: [N] {first chunk, number of chunks}
   const int2* seq_span;    // varlen: [N] {first token, length} (clamped into [0, T])
+  const int32_t* seq_order;  // varlen: [N] sequences by chunk count, longest first
   int32_t T;               // tokens per row (fixed) / packed total (varlen)
   int32_t nc_row;          // chunks per row (fixed)
   int32_t max_chunks;      // number of chunk slots
@@ -40,7 +41,8 @@ struct FwdParams {
 };
 
 hipError_t launch_sched(const int64_t* cu_seqlens, int32_t N, int32_t T, int32_t max_chunks,
-                        int2* seq_tab, int2* chunk_tab, int2* seq_span, hipStream_t stream);
+                        int2* seq_tab, int2* chunk_tab, int2* seq_span, int32_t* seq_order,
+                        hipStream_t stream);
 hipError_t launch_intra(const FwdParams& p, hipStream_t stream);
 hipError_t launch_chain(const FwdParams& p, hipStream_t stream);
 hipError_t launch_recurrent(const FwdParams& p, const int64_t* cu_seqlens, hipStream_t stream);

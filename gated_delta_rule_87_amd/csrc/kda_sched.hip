@@ -6,6 +6,9 @@
 //   seq_tab[n]   = {first chunk index, number of 64-token chunks} of sequence n
 //   seq_span[n]  = {first token, length} of sequence n (after clamping)
 //   chunk_tab[i] = {first token, length <= 64} of chunk i (length 0: unused)
+//   seq_order[k] = the sequence with the k-th most chunks (ties: lower index
+//                  first), so the sequential state chains start longest first;
+//                  input order when N > SORT_MAX
 // Chunks never straddle sequences; a sequence's last chunk may be partial.
 // Every sequence is clamped into [0, T] and the chunk count into the slot
 // budget floor(T/64) + N, so malformed contents cannot drive the other kernels
@@ -17,11 +20,14 @@ namespace kda {
 namespace {
 
 constexpr int SCHED_THREADS = 1024;
+constexpr int SORT_MAX = 4096;   // sequences sorted in LDS (bitonic); beyond: input order
 
 __global__ __launch_bounds__(SCHED_THREADS) void kda_sched_kernel(const int64_t* cu, int32_t N, int32_t T,
                                                                   int32_t max_chunks, int2* seq_tab,
-                                                                  int2* chunk_tab, int2* seq_span) {
+                                                                  int2* chunk_tab, int2* seq_span,
+                                                                  int32_t* seq_order) {
   __shared__ int32_t warp_sums[SCHED_THREADS / 64];
+  __shared__ uint64_t keys[SORT_MAX];
   __shared__ int32_t carry_s;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   if (tid == 0) carry_s = 0;
@@ -89,14 +95,42 @@ __global__ __launch_bounds__(SCHED_THREADS) void kda_sched_kernel(const int64_t*
     }
     chunk_tab[i] = e;
   }
+
+  // pass 3: longest-first order of the sequences. Key = (INT32_MAX - chunks) << 32 | n,
+  // sorted ascending by a bitonic network over the next power of two >= N.
+  if (N > SORT_MAX) {
+    for (int n = tid; n < N; n += SCHED_THREADS) seq_order[n] = n;
+    return;
+  }
+  int np = 1;
+  while (np < N) np <<= 1;
+  for (int i = tid; i < np; i += SCHED_THREADS)
+    keys[i] = i < N ? ((uint64_t)(uint32_t)(0x7fffffff - seq_tab[i].y) << 32) | (uint32_t)i : ~0ull;
+  __syncthreads();
+  for (int k = 2; k <= np; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < np; i += SCHED_THREADS) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const uint64_t a = keys[i], b = keys[ixj];
+          if ((a > b) == ((i & k) == 0)) {
+            keys[i] = b;
+            keys[ixj] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int n = tid; n < N; n += SCHED_THREADS) seq_order[n] = (int32_t)(uint32_t)keys[n];
 }
 
 }  // namespace
 
 hipError_t launch_sched(const int64_t* cu_seqlens, int32_t N, int32_t T, int32_t max_chunks, int2* seq_tab,
-                        int2* chunk_tab, int2* seq_span, hipStream_t stream) {
+                        int2* chunk_tab, int2* seq_span, int32_t* seq_order, hipStream_t stream) {
   hipLaunchKernelGGL(kda_sched_kernel, dim3(1), dim3(SCHED_THREADS), 0, stream, cu_seqlens, N, T, max_chunks,
-                     seq_tab, chunk_tab, seq_span);
+                     seq_tab, chunk_tab, seq_span, seq_order);
   return hipGetLastError();
 }
 

@@ -54,7 +54,7 @@ def test_workspace_size():
     assert kda.workspace_size(1, 100, 2) == al(2 * 2 * rec)             # ceil(100/64) = 2
     # varlen: floor(T/64) + N chunk slots, plus the tables
     ws = kda.workspace_size(1, 8192, 64, 8)
-    assert ws == al((128 + 8) * 64 * rec) + al(8 * 8) + al((128 + 8) * 8) + al(8 * 8)
+    assert ws == al((128 + 8) * 64 * rec) + al(8 * 8) + al((128 + 8) * 8) + al(8 * 8) + al(8 * 4)
     assert kda.workspace_size(1, 0, 4) == 0
     assert kda.workspace_size(0, 10, 4) == 0 and kda.workspace_size(1, -1, 4) == 0
     assert kda.workspace_size(1, 10, 0) == 0
