@@ -163,11 +163,12 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
 
   // ---------------- phase A: loads, gate, sub-chunk cumulative sums, norms ----
   u32x4 qraw[4], kraw[4], vraw[4];
-  float Gs[32];
+  float Gs[32];   // sub-chunk cumulative gates in log2 units (exp2(Gs) = exp of the natural sums)
   float rq, rk;
   {
-    const float rate = __expf(p.A_log[h]);
-    const float lb = p.lower_bound;
+    // gate * log2(e) = (lb log2 e) / (1 + 2^(-exp(A_log) log2(e) (g + dt_bias)))
+    const float rate2 = -__expf(p.A_log[h]) * LOG2E;
+    const float lb2 = p.lower_bound * LOG2E;
     const float* dt = p.dt_bias + (size_t)h * KD;
     float ssq = 0.0f, ssk = 0.0f;
 #pragma unroll
@@ -176,17 +177,18 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
       kraw[s] = load_row8(p.k + rowoff, s, gq, valid);
       vraw[s] = load_row8(p.v + rowoff, s, gq, valid);
       const u32x4 graw = load_row8(p.g + rowoff, s, gq, valid);
-      float gf[8], dtf[8], qf[8], kf[8];
+      float gf[8], dtf[8];
       unpack8(graw, gf);
-      unpack8(qraw[s], qf);
-      unpack8(kraw[s], kf);
       ld8f(dt + 32 * s + 4 * gq, dtf);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float gate = lb * sigmoidf_fast(rate * (gf[e] + dtf[e]));
-        Gs[8 * s + e] = valid ? gate : 0.0f;
-        ssq += qf[e] * qf[e];
-        ssk += kf[e] * kf[e];
+        const float gate2 = lb2 * fast_rcp(1.0f + fast_exp2(rate2 * (gf[e] + dtf[e])));
+        Gs[8 * s + e] = valid ? gate2 : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {   // squared norms straight from the packed bf16 pairs
+        ssq = dot2_bf16(qraw[s][i], qraw[s][i], ssq);
+        ssk = dot2_bf16(kraw[s][i], kraw[s][i], ssk);
       }
     }
 #pragma unroll
@@ -221,13 +223,13 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
     const float GL = t0v + t1v + t2v + t3v;
     const float rA = wa ? t0v : 0.0f, rA1 = wa ? t0v + t1v : t0v;                  // ref_wa, ref_wa+1
     const float rB = wa ? t0v + t1v + t2v : t0v + t1v, rB1 = wa ? GL : t0v + t1v + t2v;   // ref_wa+2, ref_wa+3
-    sm.exref[wa][c] = __expf(rA);
-    sm.eend[wa][c] = __expf(rA1 - rA);
-    sm.c2[wa][c] = __expf(GL - rA1);
-    sm.exref[wa + 2][c] = __expf(rB);
-    sm.eend[wa + 2][c] = __expf(rB1 - rB);
-    sm.c2[wa + 2][c] = __expf(GL - rB1);
-    if (tid < KD) reinterpret_cast<float*>(rec + OFF_GAML)[c] = __expf(GL);
+    sm.exref[wa][c] = fast_exp2(rA);   // the totals are in log2 units
+    sm.eend[wa][c] = fast_exp2(rA1 - rA);
+    sm.c2[wa][c] = fast_exp2(GL - rA1);
+    sm.exref[wa + 2][c] = fast_exp2(rB);
+    sm.eend[wa + 2][c] = fast_exp2(rB1 - rB);
+    sm.c2[wa + 2][c] = fast_exp2(GL - rB1);
+    if (tid < KD) reinterpret_cast<float*>(rec + OFF_GAML)[c] = fast_exp2(GL);
   }
   lds_barrier();
 
@@ -249,7 +251,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float kn = kf[e] * rk, qn = qf[e] * rq;
-      const float ee = fast_exp(Gs[8 * s + e]);   // <= 1
+      const float ee = fast_exp2(Gs[8 * s + e]);  // <= 1
       const float ie = fast_rcp(ee);              // <= e^80
       rke[e] = kn * ee;
       rqe[e] = qn * ee;
