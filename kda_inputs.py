@@ -66,7 +66,7 @@ def ragged_lengths(gen: torch.Generator, n: int, lo: int = 64, hi: int = 4096) -
 
 
 def workload(idx: int) -> Workload:
-    """The five named workloads (by index)."""
+    """The named workloads (by index): 0-4 prefill shapes, 5 a decode step."""
     if idx == 0:
         return Workload("tiny_T256_H2", B=1, T=256, H=2)
     if idx == 1:
@@ -80,6 +80,8 @@ def workload(idx: int) -> Workload:
                         final='bf16', lower_bound=-2.0, extra={'draw_lengths': True})
     if idx == 4:
         return Workload("batched_B4_T32768_H64", B=4, T=32768, H=64, state='fp32')
+    if idx == 5:   # one generation step: one token per sequence, state passed in and out
+        return Workload("decode_N256_H64", B=1, T=256, H=64, lengths=[1] * 256, state='fp32')
     raise ValueError(idx)
 
 

@@ -164,6 +164,18 @@ def test_full_size_sampled(idx, heads):
     check(o, f, ro, rf, w.final, w.name, heads=heads)
 
 
+@pytest.mark.parametrize("path", ["recurrent", "chunked"])
+def test_decode_step_sampled(path):
+    """One generation step (one token per sequence, fp32 state in and out), sampled heads."""
+    w = kda_inputs.workload(5)
+    heads = [0, 31, 63]
+    say(f"workload 5 {w.name} path={path} heads={heads}")
+    d = kda_inputs.make_inputs(w)
+    o, f = run(d, w, path)
+    ro, rf = oracle_for(d, heads=heads)
+    check(o, f, ro, rf, w.final, f"{w.name}/{path}", heads=heads)
+
+
 def test_batched_long_one_call_vs_chained():
     """B=4, T=32768: one call, and four chained 8192-token calls (final -> initial)."""
     w = kda_inputs.workload(4)

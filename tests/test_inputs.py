@@ -32,6 +32,8 @@ def test_named_workloads():
     assert w3.T == sum(w3.lengths) and w3.state == 'bf16' and w3.lower_bound == -2.0
     w4 = kda_inputs.workload(4)
     assert (w4.B, w4.T, w4.H, w4.state) == (4, 32768, 64, 'fp32')
+    w5 = kda_inputs.workload(5)
+    assert w5.lengths == [1] * 256 and (w5.T, w5.H, w5.state, w5.final) == (256, 64, 'fp32', 'fp32')
 
 
 def test_distribution_moments():
