@@ -51,7 +51,7 @@ def _load():
         lib.kda_oracle_fwd.restype = ctypes.c_int
         lib.kda_oracle_fwd.argtypes = [P, P, P, P, P, ctypes.c_double, P, P, ctypes.c_double, P,
                                        ctypes.c_int, P, P, P, I64, I64, I64, I64, I64, I64, P, I64,
-                                       ctypes.c_int]
+                                       ctypes.c_int, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -97,14 +97,23 @@ def _state(x):
     raise TypeError(x.dtype)
 
 
+FUSE_GATE, FUSE_QK_L2NORM, FUSE_BETA_SIGMOID = 1, 2, 4
+FUSE_ALL = 7
+
+
 def kda_oracle(q, k, v, g, beta, scale: float, A_log, dt_bias, lower_bound: float,
                initial_state=None, cu_seqlens=None, heads: Optional[Sequence[int]] = None,
-               want_final: bool = True, nthreads: int = 0):
+               want_final: bool = True, nthreads: int = 0, use_gate_in_kernel: bool = True,
+               use_qk_l2norm_in_kernel: bool = True, use_beta_sigmoid_in_kernel: bool = True):
     """fp64 reference. Tensors in the kernel's storage formats (torch or numpy).
 
     q, k, g, v: bf16 [B, T, H, 128]; beta bf16 [B, T, H]; A_log fp32 [H];
     dt_bias fp32 [H, K]; initial_state None or [nseq, H, V, K] (bf16/fp32/fp64);
     cu_seqlens None or int64 [N+1] (B must be 1); heads: subset of head ids.
+    The three switches select the fused input processing (True) or take the
+    input as already processed (False): g as the log-decay clamped into
+    [lower_bound, 0] (A_log, dt_bias may then be None), q and k as given, beta
+    as given.
 
     Returns (out fp64 [B*T, nh, V], final fp64 [nseq, nh, V, K] or None).
     ``scale`` and ``lower_bound`` are taken as the fp32 values a kernel call
@@ -116,9 +125,12 @@ def kda_oracle(q, k, v, g, beta, scale: float, A_log, dt_bias, lower_bound: floa
     V = vb.shape[-1]
     assert kb.shape == (B, T, H, K) and gb.shape == (B, T, H, K) and vb.shape == (B, T, H, V)
     assert bb.shape == (B, T, H)
-    al = _f32(A_log)
-    dt = _f32(dt_bias)
-    assert al.shape == (H,) and dt.shape == (H, K)
+    flags = ((FUSE_GATE if use_gate_in_kernel else 0) | (FUSE_QK_L2NORM if use_qk_l2norm_in_kernel else 0)
+             | (FUSE_BETA_SIGMOID if use_beta_sigmoid_in_kernel else 0))
+    al = _f32(A_log) if A_log is not None else None
+    dt = _f32(dt_bias) if dt_bias is not None else None
+    if use_gate_in_kernel:
+        assert al.shape == (H,) and dt.shape == (H, K)
     cu = None
     N = 0
     if cu_seqlens is not None:
@@ -143,19 +155,21 @@ def kda_oracle(q, k, v, g, beta, scale: float, A_log, dt_bias, lower_bound: floa
     lb = float(np.float32(lower_bound))
     rc = lib.kda_oracle_fwd(ptr(qb), ptr(kb), ptr(vb), ptr(gb), ptr(bb), sc, ptr(al), ptr(dt), lb,
                             ptr(st), code, ptr(fin), ptr(out), ptr(cu), N, B, T, H, K, V, ptr(hs),
-                            nh, int(nthreads))
+                            nh, int(nthreads), flags)
     if rc != 0:
         raise ValueError(f"kda_oracle_fwd failed with code {rc}")
     return out, fin
 
 
 def kda_oracle_numpy(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, initial_state=None,
-                     cu_seqlens=None):
+                     cu_seqlens=None, use_gate_in_kernel=True, use_qk_l2norm_in_kernel=True,
+                     use_beta_sigmoid_in_kernel=True):
     """numpy transcription of the same recurrence (tiny inputs only).
 
     Inputs as float64 numpy arrays holding the exact values: q, k, g [B,T,H,K],
     v [B,T,H,V], beta logits [B,T,H], A_log [H], dt_bias [H,K],
     initial_state [nseq,H,V,K] or None. Returns (out [B*T,H,V], final [nseq,H,V,K]).
+    The switches have the meaning documented in kda_oracle.
     """
     q, k, v, g, beta = (np.asarray(t, dtype=np.float64) for t in (q, k, v, g, beta))
     B, T, H, K = q.shape
@@ -172,12 +186,18 @@ def kda_oracle_numpy(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, initi
     for n, (t0, t1) in enumerate(bounds):
         for h in range(H):
             S = np.zeros((V, K)) if initial_state is None else np.array(initial_state[n, h], dtype=np.float64)
-            rate = np.exp(np.float64(A_log[h]))
+            rate = np.exp(np.float64(A_log[h])) if use_gate_in_kernel else 0.0
             for t in range(t0, t1):
-                qh = qf[t, h] / np.sqrt(np.dot(qf[t, h], qf[t, h]) + 1e-6)
-                kh = kf[t, h] / np.sqrt(np.dot(kf[t, h], kf[t, h]) + 1e-6)
-                b = 1.0 / (1.0 + np.exp(-bf[t, h]))
-                gate = lower_bound / (1.0 + np.exp(-rate * (gf[t, h] + dt_bias[h])))
+                if use_qk_l2norm_in_kernel:
+                    qh = qf[t, h] / np.sqrt(np.dot(qf[t, h], qf[t, h]) + 1e-6)
+                    kh = kf[t, h] / np.sqrt(np.dot(kf[t, h], kf[t, h]) + 1e-6)
+                else:
+                    qh, kh = qf[t, h], kf[t, h]
+                b = 1.0 / (1.0 + np.exp(-bf[t, h])) if use_beta_sigmoid_in_kernel else bf[t, h]
+                if use_gate_in_kernel:
+                    gate = lower_bound / (1.0 + np.exp(-rate * (gf[t, h] + dt_bias[h])))
+                else:
+                    gate = np.clip(gf[t, h], lower_bound, 0.0)
                 S = S * np.exp(gate)[None, :]
                 S = S - b * np.outer(S @ kh - vf[t, h], kh)
                 out[t, h] = scale * (S @ qh)

@@ -34,6 +34,16 @@
  *   the square root, scale applied to the read-out, and decay -> delta update
  *   -> read-out in that order.
  *
+ *   Fusion switches (the use_gate_in_kernel, use_qk_l2norm_in_kernel and
+ *   use_beta_sigmoid_in_kernel switches of page "FlashKDA：面向SM90+的高性能KDA
+ *   CUDA内核库", Q4). With a switch off the kernel takes that input already
+ *   processed (our reading, the plainest one):
+ *     gate off : gt[c] = g_t[c] itself, clamped into [lower_bound, 0] (the range
+ *                the safe gate bound guarantees for the in-kernel activation);
+ *                A_log and dt_bias are unused
+ *     norm off : q^, k^ = q, k as given
+ *     beta off : beta_t = b_t as given
+ *
  * Inputs are taken in their storage formats (bf16 as raw uint16 bits, fp32) and
  * widened exactly to fp64; every operation is done in fp64.
  */
@@ -52,6 +62,9 @@ static double bf16_bits_to_double(uint16_t h)
 }
 
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/* fusion switch bits (all set: the fully fused kernel) */
+enum { ORACLE_FUSE_GATE = 1, ORACLE_FUSE_QK_L2NORM = 2, ORACLE_FUSE_BETA_SIGMOID = 4 };
 
 /* state dtype codes for initial_state */
 enum { ORACLE_STATE_NONE = 0, ORACLE_STATE_BF16 = 1, ORACLE_STATE_FP32 = 2, ORACLE_STATE_FP64 = 3 };
@@ -74,17 +87,17 @@ static double load_state(const void *p, int dtype, size_t i)
 static void run_chain(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *g,
                       const uint16_t *beta, double scale, const float *A_log, const float *dt_bias,
                       double lower_bound, int64_t H, int64_t K, int64_t V, int64_t h,
-                      int64_t t_begin, int64_t t_end, int64_t nh, int64_t hi,
+                      int64_t t_begin, int64_t t_end, int64_t nh, int64_t hi, int flags,
                       double *S, double *out, double *work)
 {
     double *qh = work, *kh = work + K, *alpha = work + 2 * K;
-    const double rate = exp((double)A_log[h]);
+    const double rate = (flags & ORACLE_FUSE_GATE) ? exp((double)A_log[h]) : 0.0;
     for (int64_t t = t_begin; t < t_end; ++t) {
         const size_t row = (size_t)t * (size_t)H + (size_t)h;
         const uint16_t *qt = q + row * (size_t)K, *kt = k + row * (size_t)K;
         const uint16_t *gt = g + row * (size_t)K, *vt = v + row * (size_t)V;
 
-        /* L2-normalise q and k over the K channels */
+        /* L2-normalise q and k over the K channels (norm switch on) */
         double qs = 0.0, ks = 0.0;
         for (int64_t c = 0; c < K; ++c) {
             qh[c] = bf16_bits_to_double(qt[c]);
@@ -92,19 +105,29 @@ static void run_chain(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
             qs += qh[c] * qh[c];
             ks += kh[c] * kh[c];
         }
-        const double qn = sqrt(qs + 1e-6), kn = sqrt(ks + 1e-6);
-        for (int64_t c = 0; c < K; ++c) {
-            qh[c] /= qn;
-            kh[c] /= kn;
+        if (flags & ORACLE_FUSE_QK_L2NORM) {
+            const double qn = sqrt(qs + 1e-6), kn = sqrt(ks + 1e-6);
+            for (int64_t c = 0; c < K; ++c) {
+                qh[c] /= qn;
+                kh[c] /= kn;
+            }
         }
 
-        /* beta = sigmoid(logit) */
-        const double b = sigmoid(bf16_bits_to_double(beta[row]));
+        /* beta = sigmoid(logit) (beta switch on) or the given value */
+        const double braw = bf16_bits_to_double(beta[row]);
+        const double b = (flags & ORACLE_FUSE_BETA_SIGMOID) ? sigmoid(braw) : braw;
 
         /* per-channel gate, then the decay factor exp(gate) */
         for (int64_t c = 0; c < K; ++c) {
-            const double x = bf16_bits_to_double(gt[c]) + (double)dt_bias[h * K + c];
-            alpha[c] = exp(lower_bound * sigmoid(rate * x));
+            double gate;
+            if (flags & ORACLE_FUSE_GATE) {
+                const double x = bf16_bits_to_double(gt[c]) + (double)dt_bias[h * K + c];
+                gate = lower_bound * sigmoid(rate * x);
+            } else {
+                gate = bf16_bits_to_double(gt[c]);
+                gate = gate < lower_bound ? lower_bound : (gate > 0.0 ? 0.0 : gate);
+            }
+            alpha[c] = exp(gate);
         }
 
         /* S = S Diag(alpha);  S = S - b (S k^ - v) k^^T;  o = scale S q^ */
@@ -139,15 +162,21 @@ static void run_chain(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
  *   cu_seqlens   : NULL (nseq = B, rows of length T) or int64 [N+1] (B must be 1)
  *   heads        : NULL (all H heads, nh must equal H) or int32 [nh] head ids
  *   nthreads     : OpenMP threads (<= 0: runtime default)
+ *   flags        : ORACLE_FUSE_* bits (7 = fully fused); A_log and dt_bias may be
+ *                  NULL when ORACLE_FUSE_GATE is clear
  */
 int kda_oracle_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *g,
                    const uint16_t *beta, double scale, const float *A_log, const float *dt_bias,
                    double lower_bound, const void *initial_state, int state_dtype,
                    double *final_state, double *out, const int64_t *cu_seqlens, int64_t N,
                    int64_t B, int64_t T, int64_t H, int64_t K, int64_t V, const int32_t *heads,
-                   int64_t nh, int nthreads)
+                   int64_t nh, int nthreads, int flags)
 {
-    if (!q || !k || !v || !g || !beta || !A_log || !dt_bias || !out)
+    if (!q || !k || !v || !g || !beta || !out)
+        return 1;
+    if ((flags & ~7) != 0)
+        return 2;
+    if ((flags & ORACLE_FUSE_GATE) && (!A_log || !dt_bias))
         return 1;
     if (B < 1 || T < 0 || H < 1 || K < 1 || V < 1 || nh < 1)
         return 2;
@@ -191,7 +220,7 @@ int kda_oracle_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, cons
                                         ((size_t)n * (size_t)H + (size_t)h) * (size_t)(V * K) + (size_t)i)
                            : 0.0;
             run_chain(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, H, K, V, h, t0, t1, nh,
-                      hi, S, out, work);
+                      hi, flags, S, out, work);
             if (final_state)
                 memcpy(final_state + ((size_t)n * (size_t)nh + (size_t)hi) * (size_t)(V * K), S,
                        sizeof(double) * (size_t)(V * K));

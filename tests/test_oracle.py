@@ -336,3 +336,90 @@ def test_gate_parameters_indexed_per_head_and_channel():
     _, fin = kda_oracle(q, k, v, g, beta, 1.0, A_log, torch.tensor(dt), lb, initial_state=S0)
     got = np.log(fin[0] / S0[0]) / T                      # [H, V, K] per-channel gate
     np.testing.assert_allclose(got, np.broadcast_to(expect[:, None, :], got.shape), rtol=2e-7, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# fusion switches (use_gate_in_kernel / use_qk_l2norm_in_kernel /
+# use_beta_sigmoid_in_kernel off): closed forms
+# --------------------------------------------------------------------------
+def test_gate_off_pure_decay_with_clamp():
+    """Gate activation off and beta = 0: S_T = S0 exp(sum_t clamp(g_t, lb, 0)) per channel."""
+    K, V, T, H, lb = 8, 4, 5, 1, -2.0
+    rng = np.random.default_rng(21)
+    gt = np.array([-0.75, -7.0, 0.5, 0.0, -2.0, -1.5, -0.25, -3.0], np.float32)   # bf16-exact
+    g = bf(np.broadcast_to(gt, (1, T, H, K)).copy())
+    q = bf(rng.standard_normal((1, T, H, K)))
+    k = bf(rng.standard_normal((1, T, H, K)))
+    v = bf(rng.standard_normal((1, T, H, V)))
+    beta = bf(np.zeros((1, T, H)))                      # beta given directly: 0
+    S0 = rng.standard_normal((1, H, V, K))
+    out, fin = kda_oracle(q, k, v, g, beta, 0.5, None, None, lb, initial_state=S0,
+                          use_gate_in_kernel=False, use_beta_sigmoid_in_kernel=False)
+    gc = np.clip(gt.astype(np.float64), lb, 0.0)
+    np.testing.assert_allclose(fin[0, 0], S0[0, 0] * np.exp(T * gc)[None, :], rtol=1e-14)
+    qq = f64(q)[0, :, 0]
+    for t in range(T):
+        qh = qq[t] / math.sqrt(qq[t] @ qq[t] + 1e-6)
+        np.testing.assert_allclose(out[t, 0], 0.5 * (S0[0, 0] * np.exp((t + 1) * gc)[None, :]) @ qh,
+                                   rtol=1e-13, atol=1e-15)
+
+
+def _basis_case(T, seed, beta_val, norm_on, beta_logit):
+    K = V = 128
+    rng = np.random.default_rng(seed)
+    cols = rng.integers(0, K, T)
+    sign = rng.choice([-1.0, 1.0], T)
+    k = np.zeros((1, T, 1, K), np.float32)
+    k[0, np.arange(T), 0, cols] = sign
+    v = bf(rng.standard_normal((1, T, 1, V)))
+    q = bf(rng.standard_normal((1, T, 1, K)))
+    S0 = rng.standard_normal((1, 1, V, K))
+    beta = (torch.full((1, T, 1), beta_logit, dtype=torch.bfloat16) if beta_logit is not None
+            else bf(np.full((1, T, 1), beta_val)))
+    out, fin = kda_oracle(q, bf(k), v, bf(np.zeros((1, T, 1, K))), beta, 0.25, torch.zeros(1),
+                          torch.zeros(1, K), 0.0, initial_state=S0, use_qk_l2norm_in_kernel=norm_on,
+                          use_beta_sigmoid_in_kernel=beta_logit is not None)
+    return out, fin, S0, cols, sign, f64(v)[0, :, 0], f64(q)[0, :, 0]
+
+
+def test_norm_off_basis_keys_replace_columns_exactly():
+    """Norm off, beta = 1, no decay: k = +-e_c writes v into column c exactly (no 1e-6 shrink)
+    and q is read as given (not normalised)."""
+    T = 30
+    out, fin, S0, cols, sign, vv, qq = _basis_case(T, 5, None, False, float('inf'))
+    S = S0[0, 0].copy()
+    for t in range(T):
+        S[:, cols[t]] = sign[t] * vv[t]
+        np.testing.assert_allclose(out[t, 0], 0.25 * S @ qq[t], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(fin[0, 0], S, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("bval", [0.5, 0.25, 1.0])
+def test_beta_off_basis_keys_closed_form(bval):
+    """Beta given directly (b), norm on: column c <- (1 - b rho) S_c + b sign sqrt(rho) v."""
+    T = 24
+    out, fin, S0, cols, sign, vv, qq = _basis_case(T, 8, bval, True, None)
+    rho = 1.0 / (1.0 + 1e-6)
+    S = S0[0, 0].copy()
+    for t in range(T):
+        c = cols[t]
+        S[:, c] = (1 - bval * rho) * S[:, c] + bval * sign[t] * math.sqrt(rho) * vv[t]
+        qh = qq[t] / math.sqrt(qq[t] @ qq[t] + 1e-6)
+        np.testing.assert_allclose(out[t, 0], 0.25 * S @ qh, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(fin[0, 0], S, rtol=1e-12, atol=1e-14)
+
+
+def test_numpy_transcription_matches_c_with_switches_off():
+    lens = [9, 0, 14]
+    d = kda_inputs.make_inputs(kda_inputs.custom(lengths=lens, H=2, seed=17, state='fp32', lower_bound=-1.5))
+    sw = dict(use_gate_in_kernel=False, use_qk_l2norm_in_kernel=False, use_beta_sigmoid_in_kernel=False)
+    beta01 = torch.sigmoid(d['beta'].float()).to(torch.bfloat16)   # a probability-valued beta input
+    o, f = kda_oracle(d['q'], d['k'], d['v'], d['g'], beta01, d['scale'], None, None, d['lower_bound'],
+                      initial_state=d['initial_state'], cu_seqlens=d['cu_seqlens'], **sw)
+    on, fn = kda_oracle_numpy(*(f64(t) for t in (d['q'], d['k'], d['v'], d['g'], beta01)),
+                              float(np.float32(d['scale'])), None, None, float(np.float32(d['lower_bound'])),
+                              initial_state=f64(d['initial_state']), cu_seqlens=d['cu_seqlens'].numpy(), **sw)
+    # unnormalised keys (|k|^2 ~ 128) grow the state: allow for the different summation
+    # orders of numpy's dot and the C loops
+    np.testing.assert_allclose(o, on, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(f, fn, rtol=1e-10, atol=1e-12)
