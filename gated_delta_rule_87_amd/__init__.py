@@ -30,6 +30,7 @@ __all__ = ["fwd", "fwd_recurrent", "workspace_size", "lib", "KDAError", "status_
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
 STATE_NONE, STATE_BF16, STATE_FP32 = 0, 1, 2
+FUSE_GATE, FUSE_QK_L2NORM, FUSE_BETA_SIGMOID = 1, 2, 4
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE", 4: "KDA_ERR_VALUE",
            5: "KDA_ERR_ALIGN", 6: "KDA_ERR_WORKSPACE", 7: "KDA_ERR_HIP"}
 
@@ -54,6 +55,13 @@ def _setup(L):
     L.kda_fwd_recurrent.restype = I
     L.kda_fwd_recurrent.argtypes = [P, P, P, P, P, F, P, P, P, F, P, I, P, I, P, I64, I64, I64, I64, I64,
                                     I64, P]
+    U32 = ctypes.c_uint32
+    L.kda_fwd_ex.restype = I
+    L.kda_fwd_ex.argtypes = [P, P, P, P, P, F, P, P, P, F, P, I, P, I, P, I64, I64, I64, I64, I64, I64, U32, P,
+                             ctypes.c_size_t, P]
+    L.kda_fwd_recurrent_ex.restype = I
+    L.kda_fwd_recurrent_ex.argtypes = [P, P, P, P, P, F, P, P, P, F, P, I, P, I, P, I64, I64, I64, I64, I64,
+                                       I64, U32, P]
     L.kda_status_string.restype = ctypes.c_char_p
     L.kda_status_string.argtypes = [I]
     L.kda_version.restype = ctypes.c_char_p
@@ -115,7 +123,12 @@ def _state_code(t: Optional[torch.Tensor]) -> int:
     raise ValueError(f"state must be bf16 or fp32, got {t.dtype}")
 
 
-def _prepare(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens):
+def _flags(use_gate_in_kernel, use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel) -> int:
+    return ((FUSE_GATE if use_gate_in_kernel else 0) | (FUSE_QK_L2NORM if use_qk_l2norm_in_kernel else 0)
+            | (FUSE_BETA_SIGMOID if use_beta_sigmoid_in_kernel else 0))
+
+
+def _prepare(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens, gate_fused=True):
     if not isinstance(q, torch.Tensor) or q.dim() != 4:
         raise ValueError("q must be a 4-D tensor [B, T, H, K]")
     dev = q.device
@@ -130,8 +143,10 @@ def _prepare(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, 
     _check("v", v, torch.bfloat16, (B, T, H, V), dev)
     _check("beta", beta, torch.bfloat16, (B, T, H), dev)
     _check("out", out, torch.bfloat16, (B, T, H, V), dev)
-    _check("A_log", A_log, torch.float32, (H,), dev)
-    _check("dt_bias", dt_bias, torch.float32, (H, K), dev)
+    if gate_fused or A_log is not None:
+        _check("A_log", A_log, torch.float32, (H,), dev)
+    if gate_fused or dt_bias is not None:
+        _check("dt_bias", dt_bias, torch.float32, (H, K), dev)
     N = 0
     if cu_seqlens is not None:
         if B != 1:
@@ -155,32 +170,45 @@ def _stream_ptr(device) -> ctypes.c_void_p:
 
 
 def fwd(q, k, v, g, beta, scale: float, out, A_log, dt_bias, lower_bound: float,
-        initial_state=None, final_state=None, cu_seqlens=None, workspace: Optional[torch.Tensor] = None):
-    """Chunked KDA forward; writes ``out`` (and ``final_state``) in place, returns None."""
-    B, T, H, K, V, N = _prepare(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens)
+        initial_state=None, final_state=None, cu_seqlens=None, workspace: Optional[torch.Tensor] = None,
+        use_gate_in_kernel: bool = True, use_qk_l2norm_in_kernel: bool = True,
+        use_beta_sigmoid_in_kernel: bool = True):
+    """Chunked KDA forward; writes ``out`` (and ``final_state``) in place, returns None.
+
+    The three switches select the in-kernel input processing (default) or take
+    that input as already processed: g as the log-decay (clamped into
+    [lower_bound, 0]; A_log and dt_bias may be None), q and k as given, beta as
+    given (kda_fwd_ex in include/kda.h).
+    """
+    flags = _flags(use_gate_in_kernel, use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel)
+    B, T, H, K, V, N = _prepare(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens,
+                                gate_fused=use_gate_in_kernel)
     L = lib()
     ws_bytes = workspace_size(B, T, H, N)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     elif workspace.numel() * workspace.element_size() < ws_bytes or workspace.device != q.device:
         raise ValueError(f"workspace must hold {ws_bytes} bytes on {q.device}")
-    rc = L.kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(out), _ptr(A_log),
-                   _ptr(dt_bias), float(lower_bound), _ptr(initial_state), _state_code(initial_state),
-                   _ptr(final_state), _state_code(final_state), _ptr(cu_seqlens), N, B, T, H, K, V,
-                   _ptr(workspace), workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
+    rc = L.kda_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(out), _ptr(A_log),
+                      _ptr(dt_bias), float(lower_bound), _ptr(initial_state), _state_code(initial_state),
+                      _ptr(final_state), _state_code(final_state), _ptr(cu_seqlens), N, B, T, H, K, V, flags,
+                      _ptr(workspace), workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
     if rc != 0:
         raise KDAError(rc, status_string(rc))
     return None
 
 
 def fwd_recurrent(q, k, v, g, beta, scale: float, out, A_log, dt_bias, lower_bound: float,
-                  initial_state=None, final_state=None, cu_seqlens=None):
+                  initial_state=None, final_state=None, cu_seqlens=None, use_gate_in_kernel: bool = True,
+                  use_qk_l2norm_in_kernel: bool = True, use_beta_sigmoid_in_kernel: bool = True):
     """Token-by-token KDA forward (online generation / reference); same contract as fwd."""
-    B, T, H, K, V, N = _prepare(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens)
-    rc = lib().kda_fwd_recurrent(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(out),
-                                 _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state),
-                                 _state_code(initial_state), _ptr(final_state), _state_code(final_state),
-                                 _ptr(cu_seqlens), N, B, T, H, K, V, _stream_ptr(q.device))
+    flags = _flags(use_gate_in_kernel, use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel)
+    B, T, H, K, V, N = _prepare(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens,
+                                gate_fused=use_gate_in_kernel)
+    rc = lib().kda_fwd_recurrent_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(out),
+                                    _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state),
+                                    _state_code(initial_state), _ptr(final_state), _state_code(final_state),
+                                    _ptr(cu_seqlens), N, B, T, H, K, V, flags, _stream_ptr(q.device))
     if rc != 0:
         raise KDAError(rc, status_string(rc))
     return None

@@ -21,6 +21,10 @@
 
 namespace {
 
+static_assert(kda::FUSE_GATE == KDA_FUSE_GATE && kda::FUSE_QK_L2NORM == KDA_FUSE_QK_L2NORM &&
+                  kda::FUSE_BETA_SIGMOID == KDA_FUSE_BETA_SIGMOID,
+              "fusion switch values");
+
 constexpr size_t ALIGN = 256;
 
 inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
@@ -66,8 +70,12 @@ bool env_flag(const char* name) {
 int check_common(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,
                  const void* out, const float* A_log, const float* dt_bias, float lower_bound,
                  const void* initial_state, int initial_dtype, const void* final_state, int final_dtype,
-                 const int64_t* cu_seqlens, int64_t N, int64_t B, int64_t T, int64_t H, int64_t K, int64_t V) {
-  if (!q || !k || !v || !g || !beta || !out || !A_log || !dt_bias) return KDA_ERR_NULL;
+                 const int64_t* cu_seqlens, int64_t N, int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                 uint32_t flags) {
+  if (flags & ~(uint32_t)KDA_FUSE_ALL) return KDA_ERR_VALUE;
+  const bool gate_fused = (flags & KDA_FUSE_GATE) != 0;
+  if (!q || !k || !v || !g || !beta || !out) return KDA_ERR_NULL;
+  if (gate_fused && (!A_log || !dt_bias)) return KDA_ERR_NULL;
   if (K != kda::KD || V != kda::VD) return KDA_ERR_SHAPE;
   if (B < 1 || T < 0 || H < 1 || H > (1 << 20)) return KDA_ERR_SHAPE;
   if (cu_seqlens && (B != 1 || N < 1)) return KDA_ERR_SHAPE;
@@ -84,7 +92,7 @@ int check_common(const void* q, const void* k, const void* v, const void* g, con
   if (!std::isfinite(scale)) return KDA_ERR_VALUE;
   const void* a16[] = {q, k, v, g, out, A_log, dt_bias};
   for (const void* p : a16)
-    if (!aligned(p, 16)) return KDA_ERR_ALIGN;
+    if (p && !aligned(p, 16)) return KDA_ERR_ALIGN;
   if (!aligned(beta, 2)) return KDA_ERR_ALIGN;
   if (initial_state && !aligned(initial_state, 16)) return KDA_ERR_ALIGN;
   if (final_state && !aligned(final_state, 16)) return KDA_ERR_ALIGN;
@@ -106,8 +114,9 @@ int validate_cu_on_host(const int64_t* cu, int64_t N, int64_t T, hipStream_t str
 kda::FwdParams make_params(const void* q, const void* k, const void* v, const void* g, const void* beta,
                            float scale, void* out, const float* A_log, const float* dt_bias, float lower_bound,
                            const void* initial_state, int initial_dtype, void* final_state, int final_dtype,
-                           int64_t H) {
+                           int64_t H, uint32_t flags) {
   kda::FwdParams p{};
+  p.flags = flags;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);
@@ -187,8 +196,18 @@ int kda_fwd(const void* q, const void* k, const void* v, const void* g, const vo
             const float* A_log, const float* dt_bias, float lower_bound, const void* initial_state,
             int initial_dtype, void* final_state, int final_dtype, const int64_t* cu_seqlens, int64_t N, int64_t B,
             int64_t T, int64_t H, int64_t K, int64_t V, void* workspace, size_t workspace_bytes, void* stream) {
+  return kda_fwd_ex(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state, initial_dtype,
+                    final_state, final_dtype, cu_seqlens, N, B, T, H, K, V, KDA_FUSE_ALL, workspace,
+                    workspace_bytes, stream);
+}
+
+int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale, void* out,
+               const float* A_log, const float* dt_bias, float lower_bound, const void* initial_state,
+               int initial_dtype, void* final_state, int final_dtype, const int64_t* cu_seqlens, int64_t N,
+               int64_t B, int64_t T, int64_t H, int64_t K, int64_t V, uint32_t flags, void* workspace,
+               size_t workspace_bytes, void* stream) {
   int rc = check_common(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state, initial_dtype,
-                        final_state, final_dtype, cu_seqlens, N, B, T, H, K, V);
+                        final_state, final_dtype, cu_seqlens, N, B, T, H, K, V, flags);
   if (rc != KDA_OK) return rc;
   const bool varlen = cu_seqlens != nullptr;
   Layout L;
@@ -204,7 +223,7 @@ int kda_fwd(const void* q, const void* k, const void* v, const void* g, const vo
   }
 
   kda::FwdParams p = make_params(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
-                                 initial_dtype, final_state, final_dtype, H);
+                                 initial_dtype, final_state, final_dtype, H, flags);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   p.rec = ws + L.rec;
   p.map.T = (int32_t)T;
@@ -250,8 +269,18 @@ int kda_fwd_recurrent(const void* q, const void* k, const void* v, const void* g
                       const void* initial_state, int initial_dtype, void* final_state, int final_dtype,
                       const int64_t* cu_seqlens, int64_t N, int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
                       void* stream) {
+  return kda_fwd_recurrent_ex(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                              initial_dtype, final_state, final_dtype, cu_seqlens, N, B, T, H, K, V, KDA_FUSE_ALL,
+                              stream);
+}
+
+int kda_fwd_recurrent_ex(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,
+                         void* out, const float* A_log, const float* dt_bias, float lower_bound,
+                         const void* initial_state, int initial_dtype, void* final_state, int final_dtype,
+                         const int64_t* cu_seqlens, int64_t N, int64_t B, int64_t T, int64_t H, int64_t K,
+                         int64_t V, uint32_t flags, void* stream) {
   int rc = check_common(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state, initial_dtype,
-                        final_state, final_dtype, cu_seqlens, N, B, T, H, K, V);
+                        final_state, final_dtype, cu_seqlens, N, B, T, H, K, V, flags);
   if (rc != KDA_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool varlen = cu_seqlens != nullptr;
@@ -260,7 +289,7 @@ int kda_fwd_recurrent(const void* q, const void* k, const void* v, const void* g
     if (rc != KDA_OK) return rc;
   }
   kda::FwdParams p = make_params(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
-                                 initial_dtype, final_state, final_dtype, H);
+                                 initial_dtype, final_state, final_dtype, H, flags);
   p.map.T = (int32_t)T;
   p.map.nseq = (int32_t)(varlen ? N : B);
   hipError_t e = kda::launch_recurrent(p, cu_seqlens, st);

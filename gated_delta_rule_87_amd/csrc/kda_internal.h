@@ -7,6 +7,9 @@
 
 namespace kda {
 
+// fusion switches (same values as the KDA_FUSE_* constants of the public header)
+constexpr uint32_t FUSE_GATE = 1, FUSE_QK_L2NORM = 2, FUSE_BETA_SIGMOID = 4;
+
 // Where a chunk's tokens are: fixed-length rows (B rows of T tokens, chunk i is
 // row i / nc_row, piece i % nc_row) or the varlen tables built on the device.
 struct ChunkMap {
@@ -36,6 +39,7 @@ struct FwdParams {
   float scale;
   float lower_bound;
   int32_t H;
+  uint32_t flags;          // KDA_FUSE_* bits: which input processing runs in the kernels
   ChunkMap map;
   uint8_t* rec;            // chunk records: [max_chunks][H][REC_BYTES]
 };

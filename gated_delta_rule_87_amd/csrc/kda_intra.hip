@@ -166,10 +166,12 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
   float Gs[32];   // sub-chunk cumulative gates in log2 units (exp2(Gs) = exp of the natural sums)
   float rq, rk;
   {
-    // gate * log2(e) = (lb log2 e) / (1 + 2^(-exp(A_log) log2(e) (g + dt_bias)))
-    const float rate2 = -__expf(p.A_log[h]) * LOG2E;
-    const float lb2 = p.lower_bound * LOG2E;
-    const float* dt = p.dt_bias + (size_t)h * KD;
+    // fused gate: gate * log2(e) = (lb log2 e) / (1 + 2^(-exp(A_log) log2(e) (g + dt_bias)));
+    // pre-activated gate (switch off): g clamped into [lb, 0], times log2(e)
+    const bool fuse_gate = (p.flags & FUSE_GATE) != 0;
+    const float lb = p.lower_bound, lb2 = lb * LOG2E;
+    const float rate2 = fuse_gate ? -__expf(p.A_log[h]) * LOG2E : 0.0f;
+    const float* dt = fuse_gate ? p.dt_bias + (size_t)h * KD : nullptr;
     float ssq = 0.0f, ssk = 0.0f;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -177,13 +179,19 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
       kraw[s] = load_row8(p.k + rowoff, s, gq, valid);
       vraw[s] = load_row8(p.v + rowoff, s, gq, valid);
       const u32x4 graw = load_row8(p.g + rowoff, s, gq, valid);
-      float gf[8], dtf[8];
+      float gf[8];
       unpack8(graw, gf);
-      ld8f(dt + 32 * s + 4 * gq, dtf);
+      if (fuse_gate) {
+        float dtf[8];
+        ld8f(dt + 32 * s + 4 * gq, dtf);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float gate2 = lb2 * fast_rcp(1.0f + fast_exp2(rate2 * (gf[e] + dtf[e])));
-        Gs[8 * s + e] = valid ? gate2 : 0.0f;
+        for (int e = 0; e < 8; ++e) {
+          const float gate2 = lb2 * fast_rcp(1.0f + fast_exp2(rate2 * (gf[e] + dtf[e])));
+          Gs[8 * s + e] = valid ? gate2 : 0.0f;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Gs[8 * s + e] = valid ? fminf(fmaxf(gf[e], lb), 0.0f) * LOG2E : 0.0f;
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {   // squared norms straight from the packed bf16 pairs
@@ -206,11 +214,12 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
     ssq += __shfl_xor(ssq, 32, 64);
     ssk += __shfl_xor(ssk, 16, 64);
     ssk += __shfl_xor(ssk, 32, 64);
-    rq = rsqrtf(ssq + 1e-6f);
-    rk = rsqrtf(ssk + 1e-6f);
+    const bool fuse_norm = (p.flags & FUSE_QK_L2NORM) != 0;
+    rq = fuse_norm ? rsqrtf(ssq + 1e-6f) : 1.0f;
+    rk = fuse_norm ? rsqrtf(ssk + 1e-6f) : 1.0f;
     if (gq == 0) {
       const float b = valid ? bf16_to_f32(p.beta[(size_t)(t0 + tok) * H + h]) : 0.0f;
-      sm.beta[tok] = valid ? sigmoidf_fast(b) : 0.0f;
+      sm.beta[tok] = valid ? ((p.flags & FUSE_BETA_SIGMOID) ? sigmoidf_fast(b) : b) : 0.0f;
     }
   }
   lds_barrier();

@@ -56,9 +56,12 @@ __global__ __launch_bounds__(128) void kda_recurrent_kernel(FwdParams p, const i
     for (int c = 0; c < KD; ++c) S[c] = 0.0f;
   }
 
-  const float rate = expf(p.A_log[h]);
+  const bool fuse_gate = (p.flags & FUSE_GATE) != 0, fuse_norm = (p.flags & FUSE_QK_L2NORM) != 0;
+  const bool fuse_beta = (p.flags & FUSE_BETA_SIGMOID) != 0;
+  const float rate = fuse_gate ? expf(p.A_log[h]) : 0.0f;
   const float lb = p.lower_bound, scale = p.scale;
-  const float2 dt = *reinterpret_cast<const float2*>(p.dt_bias + (size_t)h * KD + 2 * lane);
+  const float2 dt = fuse_gate ? *reinterpret_cast<const float2*>(p.dt_bias + (size_t)h * KD + 2 * lane)
+                              : make_float2(0.0f, 0.0f);
   int buf = 0;
   for (int64_t t = tb; t < te; ++t, buf ^= 1) {
     const size_t row = ((size_t)t * H + h) * KD;
@@ -73,16 +76,20 @@ __global__ __launch_bounds__(128) void kda_recurrent_kernel(FwdParams p, const i
       ssq += __shfl_xor(ssq, o, 64);
       ssk += __shfl_xor(ssk, o, 64);
     }
-    const float rq = rsqrtf(ssq + 1e-6f), rk = rsqrtf(ssk + 1e-6f);
-    const float a0 = expf(lb / (1.0f + expf(-rate * (bf16_lo(gw) + dt.x))));
-    const float a1 = expf(lb / (1.0f + expf(-rate * (bf16_hi(gw) + dt.y))));
+    const float rq = fuse_norm ? rsqrtf(ssq + 1e-6f) : 1.0f, rk = fuse_norm ? rsqrtf(ssk + 1e-6f) : 1.0f;
+    // decay factors: fused gate activation, or the given log-decay clamped into [lb, 0]
+    const float a0 = fuse_gate ? expf(lb / (1.0f + expf(-rate * (bf16_lo(gw) + dt.x))))
+                               : expf(fminf(fmaxf(bf16_lo(gw), lb), 0.0f));
+    const float a1 = fuse_gate ? expf(lb / (1.0f + expf(-rate * (bf16_hi(gw) + dt.y))))
+                               : expf(fminf(fmaxf(bf16_hi(gw), lb), 0.0f));
     float* skf = reinterpret_cast<float*>(&sk[buf][w][0]);
     float* sqf = reinterpret_cast<float*>(&sq[buf][w][0]);
     float* saf = reinterpret_cast<float*>(&sa[buf][w][0]);
     skf[2 * lane] = k0 * rk; skf[2 * lane + 1] = k1 * rk;
     sqf[2 * lane] = q0 * rq; sqf[2 * lane + 1] = q1 * rq;
     saf[2 * lane] = a0; saf[2 * lane + 1] = a1;
-    const float beta = 1.0f / (1.0f + expf(-bf16_to_f32(p.beta[(size_t)t * H + h])));
+    const float braw = bf16_to_f32(p.beta[(size_t)t * H + h]);
+    const float beta = fuse_beta ? 1.0f / (1.0f + expf(-braw)) : braw;
     const float vv = bf16_to_f32(p.v[row + tid]);
     __syncthreads();
 

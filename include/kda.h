@@ -53,10 +53,31 @@ enum kda_status {
     KDA_ERR_DTYPE = 3,     /* unknown state dtype code, or initial and final state
                               given with different dtypes                           */
     KDA_ERR_VALUE = 4,     /* lower_bound outside [-5, 0] or not finite, scale not
-                              finite, bad cu_seqlens contents (KDA_VALIDATE=1 only) */
+                              finite, unknown fusion flag bits, bad cu_seqlens
+                              contents (KDA_VALIDATE=1 only)                        */
     KDA_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                      */
     KDA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than kda_fwd_workspace_size */
     KDA_ERR_HIP = 7        /* a HIP runtime call or kernel launch failed            */
+};
+
+/*
+ * Fusion switches of kda_fwd_ex / kda_fwd_recurrent_ex (the use_gate_in_kernel,
+ * use_qk_l2norm_in_kernel and use_beta_sigmoid_in_kernel switches of page
+ * "FlashKDA：面向SM90+的高性能KDA CUDA内核库", Q4). A set bit runs that input
+ * processing inside the kernels; with a bit clear the input is taken as
+ * already processed (this library's reading):
+ *   KDA_FUSE_GATE clear          g holds the log-decay g~ itself (bf16), which
+ *                                is clamped into [lower_bound, 0]; A_log and
+ *                                dt_bias are unused and may be NULL
+ *   KDA_FUSE_QK_L2NORM clear     q and k are used as given (expected unit norm)
+ *   KDA_FUSE_BETA_SIGMOID clear  beta holds beta itself (expected in [0, 1])
+ * kda_fwd and kda_fwd_recurrent are the KDA_FUSE_ALL case.
+ */
+enum kda_fuse_flags {
+    KDA_FUSE_GATE = 1,
+    KDA_FUSE_QK_L2NORM = 2,
+    KDA_FUSE_BETA_SIGMOID = 4,
+    KDA_FUSE_ALL = 7
 };
 
 /* State dtype codes for initial_state / final_state. */
@@ -127,6 +148,24 @@ int kda_fwd_recurrent(const void *q, const void *k, const void *v, const void *g
                       int initial_dtype, void *final_state, int final_dtype,
                       const int64_t *cu_seqlens, int64_t N, int64_t B, int64_t T, int64_t H,
                       int64_t K, int64_t V, void *stream);
+
+/*
+ * kda_fwd_ex, kda_fwd_recurrent_ex -- kda_fwd / kda_fwd_recurrent with the
+ * fusion switches in `flags` (KDA_FUSE_* bits; other bits: KDA_ERR_VALUE).
+ * Every other argument and rule is that of the plain entry point, except that
+ * A_log and dt_bias may be NULL when KDA_FUSE_GATE is clear.
+ */
+int kda_fwd_ex(const void *q, const void *k, const void *v, const void *g, const void *beta,
+               float scale, void *out, const float *A_log, const float *dt_bias, float lower_bound,
+               const void *initial_state, int initial_dtype, void *final_state, int final_dtype,
+               const int64_t *cu_seqlens, int64_t N, int64_t B, int64_t T, int64_t H, int64_t K,
+               int64_t V, uint32_t flags, void *workspace, size_t workspace_bytes, void *stream);
+int kda_fwd_recurrent_ex(const void *q, const void *k, const void *v, const void *g,
+                         const void *beta, float scale, void *out, const float *A_log,
+                         const float *dt_bias, float lower_bound, const void *initial_state,
+                         int initial_dtype, void *final_state, int final_dtype,
+                         const int64_t *cu_seqlens, int64_t N, int64_t B, int64_t T, int64_t H,
+                         int64_t K, int64_t V, uint32_t flags, void *stream);
 
 /* kda_status_string -- static description of a status code (never NULL). */
 const char *kda_status_string(int status);

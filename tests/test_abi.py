@@ -31,7 +31,7 @@ def test_header_symbols_exported():
     names = declared_functions()
     assert {"kda_fwd", "kda_fwd_recurrent", "kda_fwd_workspace_size", "kda_status_string",
             "kda_version", "kda_profile_start", "kda_profile_stop", "kda_profile_kernel_count",
-            "kda_profile_kernel_name"} <= set(names)
+            "kda_profile_kernel_name", "kda_fwd_ex", "kda_fwd_recurrent_ex"} <= set(names)
     L = ctypes.CDLL(kda.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"libkda.so does not export {n}"
@@ -153,3 +153,32 @@ def test_profile_hook_host_paths():
     assert L.kda_profile_stop(None, cnt, n) == ENULL
     assert L.kda_profile_stop(ms, cnt, n - 1) == ESHAPE
     assert L.kda_profile_stop(ms, cnt, n) == EVALUE      # timing was never started
+
+
+def call_ex(flags, recurrent=False, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, scale=0.088, out=FAKE, A_log=FAKE, dt_bias=FAKE,
+             lb=-5.0, init=None, idt=0, fin=None, fdt=0, cu=None, N=0, B=1, T=64, H=2, K=128, V=128,
+             ws=None, wsb=0)
+    a.update(kw)
+    L = kda.lib()
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    head = (P(a['q']), P(a['k']), P(a['v']), P(a['g']), P(a['beta']), a['scale'], P(a['out']), P(a['A_log']),
+            P(a['dt_bias']), a['lb'], P(a['init']), a['idt'], P(a['fin']), a['fdt'], P(a['cu']), a['N'], a['B'],
+            a['T'], a['H'], a['K'], a['V'], flags)
+    if recurrent:
+        return L.kda_fwd_recurrent_ex(*head, None)
+    return L.kda_fwd_ex(*head, P(a['ws']), a['wsb'], None)
+
+
+@pytest.mark.parametrize("recurrent", [False, True])
+def test_fusion_flag_validation(recurrent):
+    """Unknown flag bits are rejected; A_log/dt_bias are required only with the fused gate
+    (a later shape error shows the NULL pointers passed the pointer checks)."""
+    for bad in (8, 0x10, 0xffffffff):
+        assert call_ex(bad, recurrent) == EVALUE
+    assert call_ex(7, recurrent, A_log=None) == ENULL
+    assert call_ex(7, recurrent, dt_bias=None) == ENULL
+    assert call_ex(1, recurrent, dt_bias=None) == ENULL
+    for flags in (0, 2, 4, 6):
+        assert call_ex(flags, recurrent, A_log=None, dt_bias=None, K=64) == ESHAPE
+        assert call_ex(flags, recurrent, A_log=None, dt_bias=None, g=None) == ENULL

@@ -212,3 +212,51 @@ def test_batched_long_one_call_vs_chained():
     ro, rf = oracle_for(d, heads=heads)
     check(a.reshape(B * T, H, 128), fa, ro, rf, 'fp32', "batched one-call", heads=heads)
     check(b.reshape(B * T, H, 128), fb, ro, rf, 'fp32', "batched chained", heads=heads)
+
+
+# ---------------------------------------------------------------------------
+# fusion switches off: pre-activated gate, pre-normalised q/k, beta given directly
+def _unfused_inputs(d, gate, norm, beta):
+    """Inputs as the caller would pass them with a switch off (still bf16)."""
+    d = dict(d)
+    if not gate:   # log-decays, partly outside [lower_bound, 0] so the clamp is exercised
+        d['g'] = (d['g'].float() * 1.5 - 1.0).to(torch.bfloat16)
+        d['A_log'] = d['dt_bias'] = None
+    if not norm:   # unit rows (the delta rule needs |k| ~ 1 to stay a contraction)
+        for n in ('q', 'k'):
+            x = d[n].float()
+            d[n] = (x / x.norm(dim=-1, keepdim=True).clamp_min(1e-3)).to(torch.bfloat16)
+    if not beta:
+        d['beta'] = torch.sigmoid(d['beta'].float()).to(torch.bfloat16)
+    return d
+
+
+SWITCHES = [(False, True, True), (True, False, True), (True, True, False), (False, False, False)]
+
+
+@pytest.mark.parametrize("path", ["chunked", "recurrent"])
+@pytest.mark.parametrize("sw", SWITCHES, ids=["gate_off", "norm_off", "beta_off", "all_off"])
+@pytest.mark.parametrize("shape", [dict(B=1, T=200, H=3, state='fp32', lower_bound=-3.0),
+                                   dict(lengths=[70, 0, 130, 5], H=2, state='bf16', final='bf16')],
+                         ids=["fixed", "varlen"])
+def test_fusion_switches_off(shape, sw, path):
+    gate, norm, beta = sw
+    w = kda_inputs.custom(**shape)
+    say(f"switches gate={gate} norm={norm} beta={beta} {shape} path={path}")
+    d = _unfused_inputs(kda_inputs.make_inputs(w), gate, norm, beta)
+    kw = dict(use_gate_in_kernel=gate, use_qk_l2norm_in_kernel=norm, use_beta_sigmoid_in_kernel=beta)
+    ro, rf = kda_oracle(d['q'], d['k'], d['v'], d['g'], d['beta'], d['scale'], d['A_log'], d['dt_bias'],
+                        d['lower_bound'], initial_state=d['initial_state'], cu_seqlens=d['cu_seqlens'], **kw)
+    device = dev()
+    x = to_dev(d, device)
+    B, T, H = x['q'].shape[:3]
+    out = torch.full((B, T, H, 128), float('nan'), dtype=torch.bfloat16, device=device)
+    fin = torch.full((w.n_seqs, H, 128, 128), float('nan'),
+                     dtype=torch.float32 if w.final == 'fp32' else torch.bfloat16, device=device)
+    fn = kda.fwd if path == "chunked" else kda.fwd_recurrent
+    fn(x['q'], x['k'], x['v'], x['g'], x['beta'], x['scale'], out, x['A_log'], x['dt_bias'], x['lower_bound'],
+       initial_state=x['initial_state'], final_state=fin, cu_seqlens=x['cu_seqlens'], **kw)
+    torch.cuda.synchronize()
+    o = out.float().double().cpu().numpy().reshape(B * T, H, 128)
+    f = fin.float().double().cpu().numpy()
+    check(o, f, ro, rf, w.final, f"switches {sw}/{path}")
