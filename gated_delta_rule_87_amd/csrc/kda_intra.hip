@@ -171,22 +171,37 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
     const bool fuse_gate = (p.flags & FUSE_GATE) != 0;
     const float lb = p.lower_bound, lb2 = lb * LOG2E;
     const float rate2 = fuse_gate ? -__expf(p.A_log[h]) * LOG2E : 0.0f;
-    const float* dt = fuse_gate ? p.dt_bias + (size_t)h * KD : nullptr;
+    // every load of the phase is issued before the first use, without a per-lane branch
+    // (tokens past the chunk end read the chunk's first row and are zeroed below), so the
+    // phase waits for memory once
+    u32x4 graw[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      qraw[s] = load_row8(p.q + rowoff, s, gq, true);
+      kraw[s] = load_row8(p.k + rowoff, s, gq, true);
+      vraw[s] = load_row8(p.v + rowoff, s, gq, true);
+      graw[s] = load_row8(p.g + rowoff, s, gq, true);
+    }
+    const float braw = bf16_to_f32(p.beta[(size_t)(t0 + (valid ? tok : 0)) * H + h]);
+    float dtf[32];
+    if (fuse_gate) {
+      const float* dt = p.dt_bias + (size_t)h * KD;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) ld8f(dt + 32 * s + 4 * gq, &dtf[8 * s]);
+    }
+    if (L < CH && !valid) {   // partial chunk: rows past its end are zero
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qraw[s] = kraw[s] = vraw[s] = graw[s] = u32x4{0u, 0u, 0u, 0u};
+    }
     float ssq = 0.0f, ssk = 0.0f;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      qraw[s] = load_row8(p.q + rowoff, s, gq, valid);
-      kraw[s] = load_row8(p.k + rowoff, s, gq, valid);
-      vraw[s] = load_row8(p.v + rowoff, s, gq, valid);
-      const u32x4 graw = load_row8(p.g + rowoff, s, gq, valid);
       float gf[8];
-      unpack8(graw, gf);
+      unpack8(graw[s], gf);
       if (fuse_gate) {
-        float dtf[8];
-        ld8f(dt + 32 * s + 4 * gq, dtf);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float gate2 = lb2 * fast_rcp(1.0f + fast_exp2(rate2 * (gf[e] + dtf[e])));
+          const float gate2 = lb2 * fast_rcp(1.0f + fast_exp2(rate2 * (gf[e] + dtf[8 * s + e])));
           Gs[8 * s + e] = valid ? gate2 : 0.0f;
         }
       } else {
@@ -217,10 +232,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
     const bool fuse_norm = (p.flags & FUSE_QK_L2NORM) != 0;
     rq = fuse_norm ? rsqrtf(ssq + 1e-6f) : 1.0f;
     rk = fuse_norm ? rsqrtf(ssk + 1e-6f) : 1.0f;
-    if (gq == 0) {
-      const float b = valid ? bf16_to_f32(p.beta[(size_t)(t0 + tok) * H + h]) : 0.0f;
-      sm.beta[tok] = valid ? ((p.flags & FUSE_BETA_SIGMOID) ? sigmoidf_fast(b) : b) : 0.0f;
-    }
+    if (gq == 0) sm.beta[tok] = valid ? ((p.flags & FUSE_BETA_SIGMOID) ? sigmoidf_fast(braw) : braw) : 0.0f;
   }
   lds_barrier();
 
