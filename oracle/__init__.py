@@ -99,12 +99,14 @@ def _state(x):
 
 FUSE_GATE, FUSE_QK_L2NORM, FUSE_BETA_SIGMOID = 1, 2, 4
 FUSE_ALL = 7
+GATE_UNBOUNDED = 8
 
 
 def kda_oracle(q, k, v, g, beta, scale: float, A_log, dt_bias, lower_bound: float,
                initial_state=None, cu_seqlens=None, heads: Optional[Sequence[int]] = None,
                want_final: bool = True, nthreads: int = 0, use_gate_in_kernel: bool = True,
-               use_qk_l2norm_in_kernel: bool = True, use_beta_sigmoid_in_kernel: bool = True):
+               use_qk_l2norm_in_kernel: bool = True, use_beta_sigmoid_in_kernel: bool = True,
+               safe_gate: bool = True):
     """fp64 reference. Tensors in the kernel's storage formats (torch or numpy).
 
     q, k, g, v: bf16 [B, T, H, 128]; beta bf16 [B, T, H]; A_log fp32 [H];
@@ -113,7 +115,9 @@ def kda_oracle(q, k, v, g, beta, scale: float, A_log, dt_bias, lower_bound: floa
     The three switches select the fused input processing (True) or take the
     input as already processed (False): g as the log-decay clamped into
     [lower_bound, 0] (A_log, dt_bias may then be None), q and k as given, beta
-    as given.
+    as given. ``safe_gate=False`` drops the lower bound: the fused gate is
+    -exp(A_log) * softplus(g + dt_bias), the unfused one min(g, 0), and
+    lower_bound is not used.
 
     Returns (out fp64 [B*T, nh, V], final fp64 [nseq, nh, V, K] or None).
     ``scale`` and ``lower_bound`` are taken as the fp32 values a kernel call
@@ -126,7 +130,7 @@ def kda_oracle(q, k, v, g, beta, scale: float, A_log, dt_bias, lower_bound: floa
     assert kb.shape == (B, T, H, K) and gb.shape == (B, T, H, K) and vb.shape == (B, T, H, V)
     assert bb.shape == (B, T, H)
     flags = ((FUSE_GATE if use_gate_in_kernel else 0) | (FUSE_QK_L2NORM if use_qk_l2norm_in_kernel else 0)
-             | (FUSE_BETA_SIGMOID if use_beta_sigmoid_in_kernel else 0))
+             | (FUSE_BETA_SIGMOID if use_beta_sigmoid_in_kernel else 0) | (0 if safe_gate else GATE_UNBOUNDED))
     al = _f32(A_log) if A_log is not None else None
     dt = _f32(dt_bias) if dt_bias is not None else None
     if use_gate_in_kernel:
@@ -163,7 +167,7 @@ def kda_oracle(q, k, v, g, beta, scale: float, A_log, dt_bias, lower_bound: floa
 
 def kda_oracle_numpy(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, initial_state=None,
                      cu_seqlens=None, use_gate_in_kernel=True, use_qk_l2norm_in_kernel=True,
-                     use_beta_sigmoid_in_kernel=True):
+                     use_beta_sigmoid_in_kernel=True, safe_gate=True):
     """numpy transcription of the same recurrence (tiny inputs only).
 
     Inputs as float64 numpy arrays holding the exact values: q, k, g [B,T,H,K],
@@ -194,10 +198,14 @@ def kda_oracle_numpy(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, initi
                 else:
                     qh, kh = qf[t, h], kf[t, h]
                 b = 1.0 / (1.0 + np.exp(-bf[t, h])) if use_beta_sigmoid_in_kernel else bf[t, h]
-                if use_gate_in_kernel:
+                if use_gate_in_kernel and safe_gate:
                     gate = lower_bound / (1.0 + np.exp(-rate * (gf[t, h] + dt_bias[h])))
-                else:
+                elif use_gate_in_kernel:
+                    gate = -rate * np.logaddexp(0.0, gf[t, h] + dt_bias[h])   # -rate * softplus
+                elif safe_gate:
                     gate = np.clip(gf[t, h], lower_bound, 0.0)
+                else:
+                    gate = np.minimum(gf[t, h], 0.0)
                 S = S * np.exp(gate)[None, :]
                 S = S - b * np.outer(S @ kh - vf[t, h], kh)
                 out[t, h] = scale * (S @ qh)

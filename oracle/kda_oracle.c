@@ -44,6 +44,13 @@
  *     norm off : q^, k^ = q, k as given
  *     beta off : beta_t = b_t as given
  *
+ *   Gate without the safe bound (the safe_gate switch of the same page, Q4,
+ *   turned off). Our reading: the gate is then the plain softplus log-decay,
+ *   not bounded below, and lower_bound is not used:
+ *     gate on  : gt[c] = -exp(A_log[h]) * softplus(g_t[c] + dt_bias[h][c]),
+ *                softplus(x) = log(1 + exp(x))
+ *     gate off : gt[c] = min(g_t[c], 0)
+ *
  * Inputs are taken in their storage formats (bf16 as raw uint16 bits, fp32) and
  * widened exactly to fp64; every operation is done in fp64.
  */
@@ -63,8 +70,12 @@ static double bf16_bits_to_double(uint16_t h)
 
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 
-/* fusion switch bits (all set: the fully fused kernel) */
-enum { ORACLE_FUSE_GATE = 1, ORACLE_FUSE_QK_L2NORM = 2, ORACLE_FUSE_BETA_SIGMOID = 4 };
+/* switch bits (fusion bits all set and the unbounded bit clear: the fully fused kernel) */
+enum { ORACLE_FUSE_GATE = 1, ORACLE_FUSE_QK_L2NORM = 2, ORACLE_FUSE_BETA_SIGMOID = 4,
+       ORACLE_GATE_UNBOUNDED = 8 };
+
+/* log(1 + exp(x)) without overflow for large x */
+static double softplus(double x) { return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x)); }
 
 /* state dtype codes for initial_state */
 enum { ORACLE_STATE_NONE = 0, ORACLE_STATE_BF16 = 1, ORACLE_STATE_FP32 = 2, ORACLE_STATE_FP64 = 3 };
@@ -120,12 +131,15 @@ static void run_chain(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
         /* per-channel gate, then the decay factor exp(gate) */
         for (int64_t c = 0; c < K; ++c) {
             double gate;
+            const int unbounded = (flags & ORACLE_GATE_UNBOUNDED) != 0;
             if (flags & ORACLE_FUSE_GATE) {
                 const double x = bf16_bits_to_double(gt[c]) + (double)dt_bias[h * K + c];
-                gate = lower_bound * sigmoid(rate * x);
+                gate = unbounded ? -rate * softplus(x) : lower_bound * sigmoid(rate * x);
             } else {
                 gate = bf16_bits_to_double(gt[c]);
-                gate = gate < lower_bound ? lower_bound : (gate > 0.0 ? 0.0 : gate);
+                gate = gate > 0.0 ? 0.0 : gate;
+                if (!unbounded && gate < lower_bound)
+                    gate = lower_bound;
             }
             alpha[c] = exp(gate);
         }
@@ -162,8 +176,8 @@ static void run_chain(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
  *   cu_seqlens   : NULL (nseq = B, rows of length T) or int64 [N+1] (B must be 1)
  *   heads        : NULL (all H heads, nh must equal H) or int32 [nh] head ids
  *   nthreads     : OpenMP threads (<= 0: runtime default)
- *   flags        : ORACLE_FUSE_* bits (7 = fully fused); A_log and dt_bias may be
- *                  NULL when ORACLE_FUSE_GATE is clear
+ *   flags        : ORACLE_FUSE_* bits (7 = fully fused) and ORACLE_GATE_UNBOUNDED;
+ *                  A_log and dt_bias may be NULL when ORACLE_FUSE_GATE is clear
  */
 int kda_oracle_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *g,
                    const uint16_t *beta, double scale, const float *A_log, const float *dt_bias,
@@ -174,7 +188,7 @@ int kda_oracle_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, cons
 {
     if (!q || !k || !v || !g || !beta || !out)
         return 1;
-    if ((flags & ~7) != 0)
+    if ((flags & ~15) != 0)
         return 2;
     if ((flags & ORACLE_FUSE_GATE) && (!A_log || !dt_bias))
         return 1;

@@ -423,3 +423,99 @@ def test_numpy_transcription_matches_c_with_switches_off():
     # orders of numpy's dot and the C loops
     np.testing.assert_allclose(o, on, rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(f, fn, rtol=1e-10, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# gate without the safe bound (safe_gate off): gate = -exp(A_log) softplus(g + dt_bias),
+# or min(g, 0) when the activation is not fused; lower_bound is not used
+# --------------------------------------------------------------------------
+def _beta0_unbounded(T, K, gate_x, A_log_val, lb, S0=None):
+    H, V = 1, 4
+    g = torch.zeros(1, T, H, K, dtype=torch.bfloat16)
+    dt = torch.tensor(np.asarray(gate_x, np.float32).reshape(1, K))
+    beta = torch.full((1, T, H), float('-inf'), dtype=torch.bfloat16)
+    rng = np.random.default_rng(9)
+    q = bf(rng.standard_normal((1, T, H, K)))
+    k = bf(rng.standard_normal((1, T, H, K)))
+    v = bf(rng.standard_normal((1, T, H, V)))
+    if S0 is None:
+        S0 = rng.standard_normal((1, H, V, K))
+    out, fin = kda_oracle(q, k, v, g, beta, 0.5, torch.tensor([A_log_val], dtype=torch.float32), dt, lb,
+                          initial_state=S0, safe_gate=False)
+    return out, fin, S0
+
+
+def test_unbounded_gate_constants():
+    """softplus pinned where it has closed forms: softplus(0) = ln 2, softplus(ln 3) = ln 4,
+    softplus(-ln 3) = ln(4/3), softplus(ln(e - 1)) = 1, softplus(40) = 40 (+4e-18),
+    softplus(-40) = 4e-18; lower_bound (-0.1 here) must not cap the gate."""
+    K, T = 6, 3
+    ln3 = float(np.float32(math.log(3.0)))
+    lem1 = float(np.float32(math.log(math.e - 1.0)))
+    xs = np.array([0.0, ln3, -ln3, lem1, 40.0, -40.0], np.float32)
+    _, fin, S0 = _beta0_unbounded(T, K, xs, 0.0, -0.1)
+    sp = np.array([math.log(2.0), math.log(4.0), math.log(4.0 / 3.0), 1.0, 40.0, 0.0])
+    ratio = fin[0, 0] / S0[0, 0]
+    np.testing.assert_allclose(np.log(ratio), np.broadcast_to(-T * sp, ratio.shape), rtol=1e-7, atol=1e-15)
+    # the rate exp(A_log): A_log = ln 2 doubles the gate
+    ln2 = float(np.float32(math.log(2.0)))
+    _, fin, S0 = _beta0_unbounded(T, K, np.zeros(K, np.float32), ln2, -0.1)
+    np.testing.assert_allclose(np.log(fin[0, 0] / S0[0, 0]), -T * 2.0 * math.log(2.0), rtol=1e-7)
+
+
+def test_unbounded_gate_huge_decay_is_a_reset():
+    """gate = -1e4: exp(gate) = 0, so every token sees an empty state:
+    S_t = beta_t v_t k^_t^T and o_t = scale beta_t (k^_t . q^_t) v_t."""
+    K = V = 16
+    T, H = 7, 1
+    rng = np.random.default_rng(31)
+    q = bf(rng.standard_normal((1, T, H, K)))
+    k = bf(rng.standard_normal((1, T, H, K)))
+    v = bf(rng.standard_normal((1, T, H, V)))
+    b = bf(rng.standard_normal((1, T, H)))
+    g = torch.zeros(1, T, H, K, dtype=torch.bfloat16)
+    dt = torch.full((H, K), 1.0e4)
+    S0 = rng.standard_normal((1, H, V, K))
+    out, fin = kda_oracle(q, k, v, g, b, 0.75, torch.zeros(H), dt, -5.0, initial_state=S0, safe_gate=False)
+    qq, kk, vv, bb = f64(q)[0, :, 0], f64(k)[0, :, 0], f64(v)[0, :, 0], f64(b)[0, :, 0]
+    for t in range(T):
+        qh = qq[t] / math.sqrt(qq[t] @ qq[t] + 1e-6)
+        kh = kk[t] / math.sqrt(kk[t] @ kk[t] + 1e-6)
+        beta = 1.0 / (1.0 + math.exp(-bb[t]))
+        np.testing.assert_allclose(out[t, 0], 0.75 * beta * (kh @ qh) * vv[t], rtol=1e-12, atol=1e-15)
+        if t == T - 1:
+            np.testing.assert_allclose(fin[0, 0], beta * np.outer(vv[t], kh), rtol=1e-12, atol=1e-15)
+
+
+def test_unbounded_gate_off_is_min_zero():
+    """Activation off, no safe bound, beta = 0: S_T = S0 exp(T min(g, 0)) per channel --
+    -7 and -30 pass unclamped (the bounded reading would cap them at lower_bound)."""
+    K, V, T, H = 8, 4, 3, 1
+    rng = np.random.default_rng(23)
+    gt = np.array([-0.75, -7.0, 0.5, 0.0, -30.0, -1.5, 3.0, -0.125], np.float32)   # bf16-exact
+    g = bf(np.broadcast_to(gt, (1, T, H, K)).copy())
+    q = bf(rng.standard_normal((1, T, H, K)))
+    k = bf(rng.standard_normal((1, T, H, K)))
+    v = bf(rng.standard_normal((1, T, H, V)))
+    S0 = rng.standard_normal((1, H, V, K))
+    _, fin = kda_oracle(q, k, v, g, bf(np.zeros((1, T, H))), 0.5, None, None, -2.0, initial_state=S0,
+                        use_gate_in_kernel=False, use_beta_sigmoid_in_kernel=False, safe_gate=False)
+    np.testing.assert_allclose(fin[0, 0], S0[0, 0] * np.exp(T * np.minimum(gt.astype(np.float64), 0.0))[None, :],
+                               rtol=1e-14)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_numpy_transcription_matches_c_unbounded_gate(fused):
+    lens = [11, 0, 6]
+    d = kda_inputs.make_inputs(kda_inputs.custom(lengths=lens, H=2, seed=29, state='fp32', lower_bound=-1.0))
+    g = d['g'] if fused else (-torch.abs(d['g'].float()) * 3).to(torch.bfloat16)
+    sw = dict(use_gate_in_kernel=fused, safe_gate=False)
+    al, dt = (d['A_log'], d['dt_bias']) if fused else (None, None)
+    o, f = kda_oracle(d['q'], d['k'], d['v'], g, d['beta'], d['scale'], al, dt, d['lower_bound'],
+                      initial_state=d['initial_state'], cu_seqlens=d['cu_seqlens'], **sw)
+    on, fn = kda_oracle_numpy(*(f64(t) for t in (d['q'], d['k'], d['v'], g, d['beta'])),
+                              float(np.float32(d['scale'])), None if al is None else f64(al),
+                              None if dt is None else f64(dt), float(np.float32(d['lower_bound'])),
+                              initial_state=f64(d['initial_state']), cu_seqlens=d['cu_seqlens'].numpy(), **sw)
+    np.testing.assert_allclose(o, on, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(f, fn, rtol=1e-12, atol=1e-14)
