@@ -2,6 +2,7 @@
 """Throughput of the chunked KDA forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1] [--no-cpu]
+                    [--path chunked|recurrent] [--gate safe|unbounded]
     python bench.py --copy-calibration      # plain 1 GiB device copy, for HBM counter scaling
 
 A step is one kda_fwd call (the whole hot path: varlen scheduler when
@@ -110,6 +111,9 @@ def main():
     ap.add_argument("--workload", type=int, default=1, help="workload index (kda_inputs.workload)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--path", choices=["chunked", "recurrent"], default="chunked")
+    ap.add_argument("--gate", choices=["safe", "unbounded"], default="safe",
+                    help="safe: lower_bound * sigmoid gate (the default); unbounded: the gate without the "
+                         "safe bound, -exp(A_log) * softplus(g + dt_bias)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device copy instead (HBM counter scaling reference)")
     args = ap.parse_args()
@@ -143,15 +147,17 @@ def main():
     N = nseq if x['cu_seqlens'] is not None else 0
     ws = torch.empty(max(1, kda.workspace_size(B, T, H, N)), dtype=torch.uint8, device=dev)
 
+    safe = args.gate == "safe"
+
     def step():
         if args.path == "chunked":
             kda.fwd(x['q'], x['k'], x['v'], x['g'], x['beta'], x['scale'], out, x['A_log'], x['dt_bias'],
                     x['lower_bound'], initial_state=x['initial_state'], final_state=fin,
-                    cu_seqlens=x['cu_seqlens'], workspace=ws)
+                    cu_seqlens=x['cu_seqlens'], workspace=ws, safe_gate=safe)
         else:
             kda.fwd_recurrent(x['q'], x['k'], x['v'], x['g'], x['beta'], x['scale'], out, x['A_log'],
                               x['dt_bias'], x['lower_bound'], initial_state=x['initial_state'],
-                              final_state=fin, cu_seqlens=x['cu_seqlens'])
+                              final_state=fin, cu_seqlens=x['cu_seqlens'], safe_gate=safe)
 
     for _ in range(args.warmup):
         step()
@@ -215,14 +221,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "T": T, "H": H, "K": 128, "V": 128,
                    "varlen_seqs": N or None, "initial_state": w.state, "final_state": w.final,
-                   "lower_bound": w.lower_bound, "path": args.path},
+                   "lower_bound": w.lower_bound if safe else None, "gate": args.gate, "path": args.path},
     }
     if kernels:
         dom = max(kernels, key=lambda k: kernels[k]["avg_ms"])
         kd = kernels[dom]
         res["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": kd["alg_GBps"], "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": kd["alg_GBps"] / HBM_PEAK_GBS,
-                           "traffic": recorded_traffic(w.name, dom),
+                           "traffic": recorded_traffic(w.name, dom) if safe else None,
                            "alg_bytes_per_launch": kd["alg_bytes"], "avg_launch_ms": kd["avg_ms"]}
     else:
         res["roofline"] = {"kernel": "kda_recurrent_kernel (whole call)", "bound": "hbm", "achieved": achieved,
@@ -241,7 +247,7 @@ def main():
         t = time.perf_counter()
         kda_oracle(d['q'], d['k'], d['v'], d['g'], d['beta'], d['scale'], d['A_log'], d['dt_bias'],
                    d['lower_bound'], initial_state=d['initial_state'], cu_seqlens=d['cu_seqlens'],
-                   want_final=True, nthreads=nthr)
+                   want_final=True, nthreads=nthr, safe_gate=safe)
         dt = time.perf_counter() - t
         chains = nseq * H
         res["cpu_baseline"] = {

@@ -31,6 +31,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
 STATE_NONE, STATE_BF16, STATE_FP32 = 0, 1, 2
 FUSE_GATE, FUSE_QK_L2NORM, FUSE_BETA_SIGMOID = 1, 2, 4
+GATE_UNBOUNDED = 8
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE", 4: "KDA_ERR_VALUE",
            5: "KDA_ERR_ALIGN", 6: "KDA_ERR_WORKSPACE", 7: "KDA_ERR_HIP"}
 
@@ -123,9 +124,9 @@ def _state_code(t: Optional[torch.Tensor]) -> int:
     raise ValueError(f"state must be bf16 or fp32, got {t.dtype}")
 
 
-def _flags(use_gate_in_kernel, use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel) -> int:
+def _flags(use_gate_in_kernel, use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel, safe_gate=True) -> int:
     return ((FUSE_GATE if use_gate_in_kernel else 0) | (FUSE_QK_L2NORM if use_qk_l2norm_in_kernel else 0)
-            | (FUSE_BETA_SIGMOID if use_beta_sigmoid_in_kernel else 0))
+            | (FUSE_BETA_SIGMOID if use_beta_sigmoid_in_kernel else 0) | (0 if safe_gate else GATE_UNBOUNDED))
 
 
 def _prepare(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens, gate_fused=True):
@@ -172,15 +173,17 @@ def _stream_ptr(device) -> ctypes.c_void_p:
 def fwd(q, k, v, g, beta, scale: float, out, A_log, dt_bias, lower_bound: float,
         initial_state=None, final_state=None, cu_seqlens=None, workspace: Optional[torch.Tensor] = None,
         use_gate_in_kernel: bool = True, use_qk_l2norm_in_kernel: bool = True,
-        use_beta_sigmoid_in_kernel: bool = True):
+        use_beta_sigmoid_in_kernel: bool = True, safe_gate: bool = True):
     """Chunked KDA forward; writes ``out`` (and ``final_state``) in place, returns None.
 
     The three switches select the in-kernel input processing (default) or take
     that input as already processed: g as the log-decay (clamped into
     [lower_bound, 0]; A_log and dt_bias may be None), q and k as given, beta as
-    given (kda_fwd_ex in include/kda.h).
+    given. ``safe_gate=False`` drops the lower bound: the gate is
+    -exp(A_log) * softplus(g + dt_bias) (or min(g, 0) unfused) and lower_bound is
+    ignored (kda_fwd_ex in include/kda.h).
     """
-    flags = _flags(use_gate_in_kernel, use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel)
+    flags = _flags(use_gate_in_kernel, use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel, safe_gate)
     B, T, H, K, V, N = _prepare(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens,
                                 gate_fused=use_gate_in_kernel)
     L = lib()
@@ -200,9 +203,10 @@ def fwd(q, k, v, g, beta, scale: float, out, A_log, dt_bias, lower_bound: float,
 
 def fwd_recurrent(q, k, v, g, beta, scale: float, out, A_log, dt_bias, lower_bound: float,
                   initial_state=None, final_state=None, cu_seqlens=None, use_gate_in_kernel: bool = True,
-                  use_qk_l2norm_in_kernel: bool = True, use_beta_sigmoid_in_kernel: bool = True):
+                  use_qk_l2norm_in_kernel: bool = True, use_beta_sigmoid_in_kernel: bool = True,
+                  safe_gate: bool = True):
     """Token-by-token KDA forward (online generation / reference); same contract as fwd."""
-    flags = _flags(use_gate_in_kernel, use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel)
+    flags = _flags(use_gate_in_kernel, use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel, safe_gate)
     B, T, H, K, V, N = _prepare(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens,
                                 gate_fused=use_gate_in_kernel)
     rc = lib().kda_fwd_recurrent_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(out),

@@ -22,8 +22,8 @@
 namespace {
 
 static_assert(kda::FUSE_GATE == KDA_FUSE_GATE && kda::FUSE_QK_L2NORM == KDA_FUSE_QK_L2NORM &&
-                  kda::FUSE_BETA_SIGMOID == KDA_FUSE_BETA_SIGMOID,
-              "fusion switch values");
+                  kda::FUSE_BETA_SIGMOID == KDA_FUSE_BETA_SIGMOID && kda::GATE_UNBOUNDED == KDA_GATE_UNBOUNDED,
+              "switch values");
 
 constexpr size_t ALIGN = 256;
 
@@ -72,7 +72,7 @@ int check_common(const void* q, const void* k, const void* v, const void* g, con
                  const void* initial_state, int initial_dtype, const void* final_state, int final_dtype,
                  const int64_t* cu_seqlens, int64_t N, int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
                  uint32_t flags) {
-  if (flags & ~(uint32_t)KDA_FUSE_ALL) return KDA_ERR_VALUE;
+  if (flags & ~(uint32_t)(KDA_FUSE_ALL | KDA_GATE_UNBOUNDED)) return KDA_ERR_VALUE;
   const bool gate_fused = (flags & KDA_FUSE_GATE) != 0;
   if (!q || !k || !v || !g || !beta || !out) return KDA_ERR_NULL;
   if (gate_fused && (!A_log || !dt_bias)) return KDA_ERR_NULL;
@@ -88,7 +88,8 @@ int check_common(const void* q, const void* k, const void* v, const void* g, con
     return initial_state ? KDA_ERR_DTYPE : KDA_ERR_NULL;
   if ((final_dtype == KDA_STATE_NONE) != (final_state == nullptr)) return final_state ? KDA_ERR_DTYPE : KDA_ERR_NULL;
   if (initial_state && final_state && initial_dtype != final_dtype) return KDA_ERR_DTYPE;
-  if (!std::isfinite(lower_bound) || lower_bound < -5.0f || lower_bound > 0.0f) return KDA_ERR_VALUE;
+  if (!(flags & KDA_GATE_UNBOUNDED) && (!std::isfinite(lower_bound) || lower_bound < -5.0f || lower_bound > 0.0f))
+    return KDA_ERR_VALUE;
   if (!std::isfinite(scale)) return KDA_ERR_VALUE;
   const void* a16[] = {q, k, v, g, out, A_log, dt_bias};
   for (const void* p : a16)

@@ -119,6 +119,17 @@ __device__ __forceinline__ float max_over_groups(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// log2(1 + 2^y): softplus(y ln 2) in log2 units, without overflow for large y
+__device__ __forceinline__ float softplus_log2(float y) {
+  return fmaxf(y, 0.0f) + __builtin_amdgcn_logf(1.0f + fast_exp2(-fabsf(y)));
+}
+
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

@@ -7,8 +7,8 @@
 
 namespace kda {
 
-// fusion switches (same values as the KDA_FUSE_* constants of the public header)
-constexpr uint32_t FUSE_GATE = 1, FUSE_QK_L2NORM = 2, FUSE_BETA_SIGMOID = 4;
+// switches (same values as the KDA_FUSE_* / KDA_GATE_UNBOUNDED constants of the public header)
+constexpr uint32_t FUSE_GATE = 1, FUSE_QK_L2NORM = 2, FUSE_BETA_SIGMOID = 4, GATE_UNBOUNDED = 8;
 
 // Where a chunk's tokens are: fixed-length rows (B rows of T tokens, chunk i is
 // row i / nc_row, piece i % nc_row) or the varlen tables built on the device.
@@ -39,7 +39,7 @@ struct FwdParams {
   float scale;
   float lower_bound;
   int32_t H;
-  uint32_t flags;          // KDA_FUSE_* bits: which input processing runs in the kernels
+  uint32_t flags;          // KDA_FUSE_* bits (which input processing runs in the kernels), GATE_UNBOUNDED
   ChunkMap map;
   uint8_t* rec;            // chunk records: [max_chunks][H][REC_BYTES]
 };

@@ -133,6 +133,66 @@ __device__ __forceinline__ void solve_column_block(IntraSmem& sm, int lt, int gq
   }
 }
 
+// lane I of each 16-lane row, broadcast to the whole row (DPP row_newbcast)
+template <int I>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + I, 0xf, 0xf, false));
+}
+
+// Diagonal 16x16 gram blocks of one sub-chunk taken entry by entry, for gates of any
+// size. Lane (gq, r) holds token r and 8 channels of k^, q^ and the per-token decays
+// alpha = exp(g~) (log2 units folded in); for every token i of the sub-chunk it adds
+//   PA[i] += k^_r . k^_i E,   PQ[i] += q^_r . k^_i E,   E = exp(G_r - G_i) (i <= r)
+// over its channels. E is a running product of the decays of tokens i+1..r, restarted
+// at 1 where i >= r, so it never overflows; entries i > r are masked by the caller.
+template <int I>
+__device__ __forceinline__ void pair_step(const float* kn, const float* qn, const float* al, int lt, float* E,
+                                          float* PA, float* PQ) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if constexpr (I < 15) {   // broadcast first: a cross-lane read must not sit under a lane condition
+      const float a = row_bcast<I + 1>(al[e]);
+      E[e] = (I >= lt) ? 1.0f : E[e] * a;
+    }
+    const float kb = row_bcast<I>(kn[e]) * E[e];
+    PA[I] = fmaf(kn[e], kb, PA[I]);
+    PQ[I] = fmaf(qn[e], kb, PQ[I]);
+  }
+  if constexpr (I > 0) pair_step<I - 1>(kn, qn, al, lt, E, PA, PQ);
+}
+
+// Sums of 16 per-lane values over the four lane groups {l, l^16, l^32, l^48}, leaving
+// lane group gq with the sums of values 4gq..4gq+3 (a reduce-scatter on the gfx950
+// cross-half lane swaps: lanes 0-31 keep values 0..7 and lanes 32-63 values 8..15,
+// then the even 16-lane rows keep the first four of those and the odd rows the rest).
+__device__ __forceinline__ f32x4 reduce_scatter16(const float* P) {
+  float t[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(P[m]), __float_as_uint(P[8 + m]), false, false);
+    t[m] = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  }
+  f32x4 r;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(t[m]), __float_as_uint(t[4 + m]), false, false);
+    r[m] = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  }
+  return r;
+}
+
+// Largest sub-chunk gate sum (log2 units) for which the factorised diagonal blocks
+// stay finite: their column factor 2^-Gs is at most 2^118, and a 32-channel MFMA
+// step then sums at most 128 * 2^118 = 2^125 < FLT_MAX.
+constexpr float DIAG_RANGE2 = 118.0f;
+
+// UB = false: the safe gate, g~ in [lower_bound, 0] with lower_bound >= -5, so a
+//             16-token sub-chunk spans at most 80 natural-log units and every diagonal
+//             block is formed from the factorised operands on MFMA.
+// UB = true : the gate without the safe bound. Sub-chunks whose gate sums stay within
+//             DIAG_RANGE2 take the same MFMA path; the others form their diagonal block
+//             with pair_step (a wave-uniform choice, per sub-chunk).
+template <bool UB>
 __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
   __shared__ IntraSmem sm;
   const int H = p.H;
@@ -165,12 +225,18 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
   u32x4 qraw[4], kraw[4], vraw[4];
   float Gs[32];   // sub-chunk cumulative gates in log2 units (exp2(Gs) = exp of the natural sums)
   float rq, rk;
+  bool slow = false;   // (UB only) this sub-chunk's diagonal block is formed entry by entry
+  // diagonal gram block of this sub-chunk: D[r][i] = k^_r.k^_i exp(Gs_r - Gs_i) and
+  // D[i][r] = k^_i.q^_r exp(Gs_r - Gs_i) in D layout (MFMA path, phase B); on the
+  // entry-by-entry path (phase A) aD holds the first transposed, see phase D
+  f32x4 aD = {0, 0, 0, 0}, qD = {0, 0, 0, 0};
   {
-    // fused gate: gate * log2(e) = (lb log2 e) / (1 + 2^(-exp(A_log) log2(e) (g + dt_bias)));
-    // pre-activated gate (switch off): g clamped into [lb, 0], times log2(e)
+    // fused safe gate: gate * log2(e) = (lb log2 e) / (1 + 2^(-exp(A_log) log2(e) (g + dt_bias)));
+    // fused unbounded gate: gate * log2(e) = -exp(A_log) log2(1 + 2^((g + dt_bias) log2 e));
+    // pre-activated gate (switch off): g clamped into [lb, 0] (unbounded: min(g, 0)), times log2(e)
     const bool fuse_gate = (p.flags & FUSE_GATE) != 0;
     const float lb = p.lower_bound, lb2 = lb * LOG2E;
-    const float rate2 = fuse_gate ? -__expf(p.A_log[h]) * LOG2E : 0.0f;
+    const float rate2 = fuse_gate ? -__expf(p.A_log[h]) * (UB ? 1.0f : LOG2E) : 0.0f;
     // every load of the phase is issued before the first use, without a per-lane branch
     // (tokens past the chunk end read the chunk's first row and are zeroed below), so the
     // phase waits for memory once
@@ -201,12 +267,14 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
       if (fuse_gate) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float gate2 = lb2 * fast_rcp(1.0f + fast_exp2(rate2 * (gf[e] + dtf[8 * s + e])));
+          const float gate2 = UB ? rate2 * softplus_log2((gf[e] + dtf[8 * s + e]) * LOG2E)
+                                 : lb2 * fast_rcp(1.0f + fast_exp2(rate2 * (gf[e] + dtf[8 * s + e])));
           Gs[8 * s + e] = valid ? gate2 : 0.0f;
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) Gs[8 * s + e] = valid ? fminf(fmaxf(gf[e], lb), 0.0f) * LOG2E : 0.0f;
+        for (int e = 0; e < 8; ++e)
+          Gs[8 * s + e] = valid ? (UB ? fminf(gf[e], 0.0f) : fminf(fmaxf(gf[e], lb), 0.0f)) * LOG2E : 0.0f;
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {   // squared norms straight from the packed bf16 pairs
@@ -216,6 +284,12 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
     }
 #pragma unroll
     for (int i = 0; i < 32; ++i) Gs[i] = row16_inclusive_scan(Gs[i]);
+    if (UB) {   // the gates are <= 0, so the smallest cumulative sum is the sub-chunk total
+      float mn = Gs[0];
+#pragma unroll
+      for (int i = 1; i < 32; ++i) mn = fminf(mn, Gs[i]);
+      slow = __builtin_amdgcn_readfirstlane(wave_min(mn) < -DIAG_RANGE2 ? 1 : 0) != 0;
+    }
     if (lt == 15) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -233,6 +307,31 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
     rq = fuse_norm ? rsqrtf(ssq + 1e-6f) : 1.0f;
     rk = fuse_norm ? rsqrtf(ssk + 1e-6f) : 1.0f;
     if (gq == 0) sm.beta[tok] = valid ? ((p.flags & FUSE_BETA_SIGMOID) ? sigmoidf_fast(braw) : braw) : 0.0f;
+    if (UB && slow) {
+      float PA[16], PQ[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) PA[i] = PQ[i] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        float qf[8], kf[8], kn[8], qn[8], al[8], E[8];
+        unpack8(qraw[s], qf);
+        unpack8(kraw[s], kf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kn[e] = kf[e] * rk;
+          qn[e] = qf[e] * rq;
+          // this token's decay: the step of the cumulative sum from the previous token
+          const float prev = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(Gs[8 * s + e]), 0x111, 0xf, 0xf, true));
+          al[e] = fast_exp2(Gs[8 * s + e] - prev);
+          E[e] = 1.0f;
+        }
+        pair_step<15>(kn, qn, al, lt, E, PA, PQ);
+      }
+      // lane (gq, r) now holds, for columns i = 4gq + j: gram row r (aD) and Aqk of
+      // query r, key i (qD, already the MFMA layout)
+      aD = reduce_scatter16(PA);
+      qD = reduce_scatter16(PQ);
+    }
   }
   lds_barrier();
 
@@ -259,7 +358,6 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
   const u32x4 idb0 = perm_operand(lt, gq, 0, 0x3F80u), idb1 = perm_operand(lt, gq, 1, 0x3F80u);
   const int half = (w & 1) * 8;   // byte offset of this sub-chunk's tokens inside a 32-token fragment
   u32x4 Rkh[4], Rqh[4];            // off-diagonal gram rows (fp16), kept for phase D
-  f32x4 aD = {0, 0, 0, 0}, qD = {0, 0, 0, 0};
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     float qf[8], kf[8], exr[8], een[8], cc2[8];
@@ -269,22 +367,39 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
     ld8f(&sm.eend[w][32 * s + 4 * gq], een);
     ld8f(&sm.c2[w][32 * s + 4 * gq], cc2);
     float rke[8], rqe[8], cki[8], tk[8], kp[8], kg[8], qg[8];
+    if (UB && slow) {   // diagonal block done in phase A; no 2^-Gs factor here
+      float tot[8], kn[8], qn[8];
+      ld8f(&sm.tot[w][32 * s + 4 * gq], tot);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float kn = kf[e] * rk, qn = qf[e] * rq;
-      const float ee = fast_exp2(Gs[8 * s + e]);  // <= 1
-      const float ie = fast_rcp(ee);              // <= e^80
-      rke[e] = kn * ee;
-      rqe[e] = qn * ee;
-      cki[e] = kn * ie;
-      tk[e] = kn * (ie * een[e]);                 // K^ exp(end_w - G) <= 1
-      kp[e] = tk[e] * cc2[e];                     // K^ exp(G_L - G)   <= 1
-      kg[e] = rke[e] * exr[e];                    // K^ exp(G)         <= 1
-      qg[e] = rqe[e] * exr[e];                    // Q^ exp(G)         <= 1
+      for (int e = 0; e < 8; ++e) {
+        kn[e] = kf[e] * rk;
+        qn[e] = qf[e] * rq;
+        const float ee = fast_exp2(Gs[8 * s + e]);   // <= 1 (may underflow to 0)
+        rke[e] = kn[e] * ee;
+        rqe[e] = qn[e] * ee;
+        tk[e] = kn[e] * fast_exp2(tot[e] - Gs[8 * s + e]);   // K^ exp(end_w - G) <= 1
+        kp[e] = tk[e] * cc2[e];
+        kg[e] = rke[e] * exr[e];
+        qg[e] = rqe[e] * exr[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float kn = kf[e] * rk, qn = qf[e] * rq;
+        const float ee = fast_exp2(Gs[8 * s + e]);  // <= 1
+        const float ie = fast_rcp(ee);              // <= e^80 (2^118 with an unbounded gate)
+        rke[e] = kn * ee;
+        rqe[e] = qn * ee;
+        cki[e] = kn * ie;
+        tk[e] = kn * (ie * een[e]);                 // K^ exp(end_w - G) <= 1
+        kp[e] = tk[e] * cc2[e];                     // K^ exp(G_L - G)   <= 1
+        kg[e] = rke[e] * exr[e];                    // K^ exp(G)         <= 1
+        qg[e] = rqe[e] * exr[e];                    // Q^ exp(G)         <= 1
+      }
+      const u32x4 rkd = pk_bf16(rke), ckd = pk_bf16(cki), rqd = pk_bf16(rqe);
+      aD = mfma_bf16(rkd, ckd, aD);                 // D[r][i] = k^_r.k^_i exp(Gs_r - Gs_i)
+      qD = mfma_bf16(ckd, rqd, qD);                 // D[i][r] = k^_i.q^_r exp(Gs_r - Gs_i)
     }
-    const u32x4 rkd = pk_bf16(rke), ckd = pk_bf16(cki), rqd = pk_bf16(rqe);
-    aD = mfma_bf16(rkd, ckd, aD);                 // D[r][i] = k^_r.k^_i exp(Gs_r - Gs_i)
-    qD = mfma_bf16(ckd, rqd, qD);                 // D[i][r] = k^_i.q^_r exp(Gs_r - Gs_i)
     Rkh[s] = pk_f16(rke);
     Rqh[s] = pk_f16(rqe);
     sm.u.tk[w][s][l] = pk_f16(tk);
@@ -345,10 +460,16 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
     }
     // rows r = 16w + 4gq + j, columns i = 16b + lt
     const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.beta[16 * w + 4 * gq]);
+    if (UB && slow) {   // aD[j] = gram[lt][4gq + j]
+      const float b = sm.beta[16 * w + lt];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 4 * gq + j;
-      sm.A[16 * w + r][16 * w + lt] = (r > lt) ? br[j] * aD[j] : 0.0f;
+      for (int j = 0; j < 4; ++j) sm.A[16 * w + lt][16 * w + 4 * gq + j] = (lt > 4 * gq + j) ? b * aD[j] : 0.0f;
+    } else {            // aD[j] = gram[4gq + j][lt]
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * gq + j;
+        sm.A[16 * w + r][16 * w + lt] = (r > lt) ? br[j] * aD[j] : 0.0f;
+      }
     }
 #pragma unroll
     for (int d = 0; d < 3; ++d) {
@@ -469,7 +590,10 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
 hipError_t launch_intra(const FwdParams& p, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.map.max_chunks * p.H;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kda_intra_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  if (p.flags & GATE_UNBOUNDED)
+    hipLaunchKernelGGL(kda_intra_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(kda_intra_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -16,6 +16,12 @@
 namespace kda {
 namespace {
 
+__device__ __forceinline__ float decay(float g, float dt, float rate, float lb, bool fuse_gate, bool unbounded) {
+  if (fuse_gate)
+    return unbounded ? fast_exp2(-rate * softplus_log2((g + dt) * LOG2E)) : expf(lb / (1.0f + expf(-rate * (g + dt))));
+  return expf(unbounded ? fminf(g, 0.0f) : fminf(fmaxf(g, lb), 0.0f));
+}
+
 __global__ __launch_bounds__(128) void kda_recurrent_kernel(FwdParams p, const int64_t* cu) {
   __shared__ f32x4 sk[2][2][KD / 4], sq[2][2][KD / 4], sa[2][2][KD / 4];   // [buffer][wave][channel/4]
   const int H = p.H;
@@ -57,7 +63,7 @@ __global__ __launch_bounds__(128) void kda_recurrent_kernel(FwdParams p, const i
   }
 
   const bool fuse_gate = (p.flags & FUSE_GATE) != 0, fuse_norm = (p.flags & FUSE_QK_L2NORM) != 0;
-  const bool fuse_beta = (p.flags & FUSE_BETA_SIGMOID) != 0;
+  const bool fuse_beta = (p.flags & FUSE_BETA_SIGMOID) != 0, unbounded = (p.flags & GATE_UNBOUNDED) != 0;
   const float rate = fuse_gate ? expf(p.A_log[h]) : 0.0f;
   const float lb = p.lower_bound, scale = p.scale;
   const float2 dt = fuse_gate ? *reinterpret_cast<const float2*>(p.dt_bias + (size_t)h * KD + 2 * lane)
@@ -77,11 +83,11 @@ __global__ __launch_bounds__(128) void kda_recurrent_kernel(FwdParams p, const i
       ssk += __shfl_xor(ssk, o, 64);
     }
     const float rq = fuse_norm ? rsqrtf(ssq + 1e-6f) : 1.0f, rk = fuse_norm ? rsqrtf(ssk + 1e-6f) : 1.0f;
-    // decay factors: fused gate activation, or the given log-decay clamped into [lb, 0]
-    const float a0 = fuse_gate ? expf(lb / (1.0f + expf(-rate * (bf16_lo(gw) + dt.x))))
-                               : expf(fminf(fmaxf(bf16_lo(gw), lb), 0.0f));
-    const float a1 = fuse_gate ? expf(lb / (1.0f + expf(-rate * (bf16_hi(gw) + dt.y))))
-                               : expf(fminf(fmaxf(bf16_hi(gw), lb), 0.0f));
+    // decay factors exp(g~): fused gate activation (safe: lb sigmoid(rate x); unbounded:
+    // -rate softplus(x), as 2^(-rate log2(1 + 2^(x log2 e)))), or the given log-decay
+    // clamped into [lb, 0] (unbounded: min(g, 0))
+    const float a0 = decay(bf16_lo(gw), dt.x, rate, lb, fuse_gate, unbounded);
+    const float a1 = decay(bf16_hi(gw), dt.y, rate, lb, fuse_gate, unbounded);
     float* skf = reinterpret_cast<float*>(&sk[buf][w][0]);
     float* sqf = reinterpret_cast<float*>(&sq[buf][w][0]);
     float* saf = reinterpret_cast<float*>(&sa[buf][w][0]);

@@ -52,8 +52,8 @@ enum kda_status {
                               cu_seqlens, N < 1 with cu_seqlens, size overflow      */
     KDA_ERR_DTYPE = 3,     /* unknown state dtype code, or initial and final state
                               given with different dtypes                           */
-    KDA_ERR_VALUE = 4,     /* lower_bound outside [-5, 0] or not finite, scale not
-                              finite, unknown fusion flag bits, bad cu_seqlens
+    KDA_ERR_VALUE = 4,     /* lower_bound outside [-5, 0] or not finite (safe gate),
+                              scale not finite, unknown flag bits, bad cu_seqlens
                               contents (KDA_VALIDATE=1 only)                        */
     KDA_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                      */
     KDA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than kda_fwd_workspace_size */
@@ -71,13 +71,23 @@ enum kda_status {
  *                                dt_bias are unused and may be NULL
  *   KDA_FUSE_QK_L2NORM clear     q and k are used as given (expected unit norm)
  *   KDA_FUSE_BETA_SIGMOID clear  beta holds beta itself (expected in [0, 1])
- * kda_fwd and kda_fwd_recurrent are the KDA_FUSE_ALL case.
+ * KDA_GATE_UNBOUNDED is the safe_gate switch of the same page turned off. The
+ * safe gate (bit clear) is the lower_bound form documented at kda_fwd; with the
+ * bit set the gate is the plain softplus log-decay, not bounded below, and
+ * lower_bound is neither used nor checked (this library's reading):
+ *   KDA_FUSE_GATE set            g~ = -exp(A_log[h]) * log(1 + exp(g + dt_bias[h]))
+ *   KDA_FUSE_GATE clear          g~ = min(g, 0)
+ * Chunks whose 16-token gate sums stay above -80 (natural log) take the same
+ * kernel path as the safe gate; others compute their diagonal 16x16 decay
+ * blocks pairwise, which costs extra vector work for those chunks only.
+ * kda_fwd and kda_fwd_recurrent are the KDA_FUSE_ALL case (safe gate).
  */
 enum kda_fuse_flags {
     KDA_FUSE_GATE = 1,
     KDA_FUSE_QK_L2NORM = 2,
     KDA_FUSE_BETA_SIGMOID = 4,
-    KDA_FUSE_ALL = 7
+    KDA_FUSE_ALL = 7,
+    KDA_GATE_UNBOUNDED = 8
 };
 
 /* State dtype codes for initial_state / final_state. */
@@ -151,9 +161,10 @@ int kda_fwd_recurrent(const void *q, const void *k, const void *v, const void *g
 
 /*
  * kda_fwd_ex, kda_fwd_recurrent_ex -- kda_fwd / kda_fwd_recurrent with the
- * fusion switches in `flags` (KDA_FUSE_* bits; other bits: KDA_ERR_VALUE).
- * Every other argument and rule is that of the plain entry point, except that
- * A_log and dt_bias may be NULL when KDA_FUSE_GATE is clear.
+ * switches in `flags` (KDA_FUSE_* bits and KDA_GATE_UNBOUNDED; other bits:
+ * KDA_ERR_VALUE). Every other argument and rule is that of the plain entry
+ * point, except that A_log and dt_bias may be NULL when KDA_FUSE_GATE is
+ * clear, and lower_bound is ignored when KDA_GATE_UNBOUNDED is set.
  */
 int kda_fwd_ex(const void *q, const void *k, const void *v, const void *g, const void *beta,
                float scale, void *out, const float *A_log, const float *dt_bias, float lower_bound,

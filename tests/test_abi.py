@@ -174,7 +174,7 @@ def call_ex(flags, recurrent=False, **kw):
 def test_fusion_flag_validation(recurrent):
     """Unknown flag bits are rejected; A_log/dt_bias are required only with the fused gate
     (a later shape error shows the NULL pointers passed the pointer checks)."""
-    for bad in (8, 0x10, 0xffffffff):
+    for bad in (0x10, 0x20, 0xffffffff):
         assert call_ex(bad, recurrent) == EVALUE
     assert call_ex(7, recurrent, A_log=None) == ENULL
     assert call_ex(7, recurrent, dt_bias=None) == ENULL
@@ -182,3 +182,13 @@ def test_fusion_flag_validation(recurrent):
     for flags in (0, 2, 4, 6):
         assert call_ex(flags, recurrent, A_log=None, dt_bias=None, K=64) == ESHAPE
         assert call_ex(flags, recurrent, A_log=None, dt_bias=None, g=None) == ENULL
+
+
+@pytest.mark.parametrize("recurrent", [False, True])
+def test_unbounded_gate_skips_lower_bound_check(recurrent):
+    """lower_bound is checked only for the safe gate: with KDA_GATE_UNBOUNDED an
+    out-of-range or NaN value passes (the later shape error shows the value check passed)."""
+    for lb in (-7.0, 1.0, float("nan")):
+        assert call_ex(7, recurrent, lb=lb) == EVALUE
+        assert call_ex(7 | 8, recurrent, lb=lb, K=64) == ESHAPE
+        assert call_ex(8, recurrent, lb=lb, A_log=None, dt_bias=None, K=64) == ESHAPE

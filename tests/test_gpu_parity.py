@@ -260,3 +260,81 @@ def test_fusion_switches_off(shape, sw, path):
     o = out.float().double().cpu().numpy().reshape(B * T, H, 128)
     f = fin.float().double().cpu().numpy()
     check(o, f, ro, rf, w.final, f"switches {sw}/{path}")
+
+
+# ---------------------------------------------------------------------------
+# gate without the safe bound (safe_gate off): -exp(A_log) softplus(g + dt_bias), or
+# min(g, 0) unfused. The regimes steer the 16-token gate sums: "mild" keeps every
+# sub-chunk on the factorised MFMA path, "strong" and "unfused" push most sub-chunks
+# past it (entry-by-entry diagonal blocks), "mixed" puts huge and tiny per-channel
+# gates in the same sub-chunks and mixes both kinds of heads.
+def _unbounded_inputs(d, regime):
+    d = dict(d)
+    H, K = d['dt_bias'].shape
+    if regime == "mild":
+        d['A_log'] = torch.full((H,), -3.5)
+    elif regime == "mixed":
+        al = torch.full((H,), math.log(16.0))
+        al[0::2] = -3.0
+        d['A_log'] = al
+        dt = d['dt_bias'].clone()
+        dt[:, 0::2] += 6.0     # softplus ~ 6: about -96 per token at rate 16
+        dt[:, 1::2] -= 6.0     # softplus ~ 0.0025
+        d['dt_bias'] = dt
+    elif regime == "unfused":
+        d['g'] = (-d['g'].float().abs() * 12.0).to(torch.bfloat16)
+        d['A_log'] = d['dt_bias'] = None
+    return d
+
+
+@pytest.mark.parametrize("path", ["chunked", "recurrent"])
+@pytest.mark.parametrize("regime", ["mild", "strong", "mixed", "unfused"])
+@pytest.mark.parametrize("shape", [dict(B=1, T=200, H=3, state='fp32', lower_bound=-3.0),
+                                   dict(lengths=[70, 0, 130, 5, 64], H=2, state='bf16', final='bf16')],
+                         ids=["fixed", "varlen"])
+def test_unbounded_gate(shape, regime, path):
+    w = kda_inputs.custom(**shape)
+    say(f"unbounded gate regime={regime} {shape} path={path}")
+    d = _unbounded_inputs(kda_inputs.make_inputs(w), regime)
+    kw = dict(use_gate_in_kernel=regime != "unfused", safe_gate=False)
+    ro, rf = kda_oracle(d['q'], d['k'], d['v'], d['g'], d['beta'], d['scale'], d['A_log'], d['dt_bias'],
+                        d['lower_bound'], initial_state=d['initial_state'], cu_seqlens=d['cu_seqlens'], **kw)
+    device = dev()
+    x = to_dev(d, device)
+    B, T, H = x['q'].shape[:3]
+    out = torch.full((B, T, H, 128), float('nan'), dtype=torch.bfloat16, device=device)
+    fin = torch.full((w.n_seqs, H, 128, 128), float('nan'),
+                     dtype=torch.float32 if w.final == 'fp32' else torch.bfloat16, device=device)
+    fn = kda.fwd if path == "chunked" else kda.fwd_recurrent
+    # lower_bound is ignored by this gate: pass a value the safe gate would reject
+    fn(x['q'], x['k'], x['v'], x['g'], x['beta'], x['scale'], out, x['A_log'], x['dt_bias'], -9.0,
+       initial_state=x['initial_state'], final_state=fin, cu_seqlens=x['cu_seqlens'], **kw)
+    torch.cuda.synchronize()
+    o = out.float().double().cpu().numpy().reshape(B * T, H, 128)
+    f = fin.float().double().cpu().numpy()
+    check(o, f, ro, rf, w.final, f"unbounded {regime}/{path}")
+
+
+@pytest.mark.parametrize("regime", ["strong", "mixed"])
+def test_unbounded_gate_full_size_sampled(regime):
+    """T=8192, H=64 (the prefill workload's shape and launch) with the unbounded gate,
+    checked on sampled heads."""
+    w = kda_inputs.workload(1)
+    heads = [0, 1, 40, 63]
+    say(f"workload 1 with the unbounded gate ({regime}): oracle on heads {heads}")
+    d = _unbounded_inputs(kda_inputs.make_inputs(w), regime)
+    ro, rf = kda_oracle(d['q'], d['k'], d['v'], d['g'], d['beta'], d['scale'], d['A_log'], d['dt_bias'],
+                        d['lower_bound'], initial_state=d['initial_state'], cu_seqlens=d['cu_seqlens'],
+                        heads=heads, safe_gate=False)
+    device = dev()
+    x = to_dev(d, device)
+    B, T, H = x['q'].shape[:3]
+    out = torch.empty((B, T, H, 128), dtype=torch.bfloat16, device=device)
+    fin = torch.empty((w.n_seqs, H, 128, 128), dtype=torch.float32, device=device)
+    kda.fwd(x['q'], x['k'], x['v'], x['g'], x['beta'], x['scale'], out, x['A_log'], x['dt_bias'],
+            x['lower_bound'], initial_state=x['initial_state'], final_state=fin, cu_seqlens=x['cu_seqlens'],
+            safe_gate=False)
+    torch.cuda.synchronize()
+    o = out.float().double().cpu().numpy().reshape(B * T, H, 128)
+    f = fin.float().double().cpu().numpy()
+    check(o, f, ro, rf, 'fp32', f"workload 1 unbounded {regime}", heads=heads)

@@ -73,3 +73,21 @@ def test_chain_lds_dma_has_uniform_destination(tmp_path):
     for i, ln in enumerate(lines):
         if ln.startswith("s_xor_b64 exec, exec"):
             raise AssertionError(f"waterfall loop (s_xor_b64 exec) at asm line {i}")
+
+
+def test_no_kernel_uses_scratch(tmp_path):
+    """Every kernel keeps its working set in registers and LDS: no VGPR spills and no
+    private (scratch) segment. A cross-lane read evaluated under a lane condition (for
+    example a DPP broadcast inside one arm of ?:) once turned into divergent branches
+    and about a thousand spilled registers."""
+    bad = []
+    for src in ("kda_intra.hip", "kda_chain.hip", "kda_sched.hip", "kda_recurrent.hip"):
+        text = "\n".join(_device_asm(src, tmp_path))
+        names = re.findall(r"\.name:\s+(\S+)", text)
+        spills = [int(x) for x in re.findall(r"\.vgpr_spill_count:\s+(\d+)", text)]
+        priv = [int(x) for x in re.findall(r"\.private_segment_fixed_size:\s+(\d+)", text)]
+        assert spills and len(spills) == len(priv)
+        for i, (sp, pr) in enumerate(zip(spills, priv)):
+            if sp or pr:
+                bad.append(f"{src}: kernel {i} ({names[i] if i < len(names) else '?'}): {sp} spills, {pr} B scratch")
+    assert not bad, "\n".join(bad)
