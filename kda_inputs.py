@@ -131,6 +131,41 @@ def make_inputs(w: Workload) -> dict:
     return d
 
 
+def make_inputs_device(w: Workload, device) -> dict:
+    """The same distributions drawn directly on ``device`` with a seeded device
+    generator, slab by slab, for sizes the host should not hold. Draw order as in
+    make_inputs; the values differ from make_inputs' (another generator)."""
+    gen = torch.Generator(device=device).manual_seed(w.seed)
+    B, T, H, K, V = w.B, w.T, w.H, w.K, w.V
+
+    def normal_bf16(shape):
+        out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        for t0 in range(0, shape[1], SLAB):
+            t1 = min(shape[1], t0 + SLAB)
+            sl = (shape[0], t1 - t0) + tuple(shape[2:])
+            out[:, t0:t1] = torch.randn(sl, generator=gen, dtype=torch.float32, device=device).to(torch.bfloat16)
+        return out
+
+    d = {'q': normal_bf16((B, T, H, K)), 'k': normal_bf16((B, T, H, K)), 'v': normal_bf16((B, T, H, V)),
+         'g': normal_bf16((B, T, H, K)), 'beta': normal_bf16((B, T, H))}
+    d['A_log'] = torch.rand(H, generator=gen, dtype=torch.float32, device=device) * math.log(16.0)
+    d['dt_bias'] = torch.randn(H, K, generator=gen, dtype=torch.float32, device=device) * 0.1
+    if w.state is not None:
+        s = torch.randn(w.n_seqs, H, V, K, generator=gen, dtype=torch.float32, device=device) * 0.02
+        d['initial_state'] = s.to(torch.bfloat16) if w.state == 'bf16' else s
+    else:
+        d['initial_state'] = None
+    d['cu_seqlens'] = None
+    if w.lengths is not None:
+        cu = [0]
+        for L in w.lengths:
+            cu.append(cu[-1] + L)
+        d['cu_seqlens'] = torch.tensor(cu, dtype=torch.int64, device=device)
+    d['scale'] = float(w.scale)
+    d['lower_bound'] = float(w.lower_bound)
+    return d
+
+
 def custom(B=1, T=64, H=1, lengths=None, state=None, final='fp32', lower_bound=-5.0, seed=0,
            scale=None, K=K_DIM, V=V_DIM) -> Workload:
     """A small workload of the same distributions (for parity and edge cases)."""

@@ -338,3 +338,31 @@ def test_unbounded_gate_full_size_sampled(regime):
     o = out.float().double().cpu().numpy().reshape(B * T, H, 128)
     f = fin.float().double().cpu().numpy()
     check(o, f, ro, rf, 'fp32', f"workload 1 unbounded {regime}", heads=heads)
+
+
+# ---------------------------------------------------------------------------
+# more than 2^31 elements per input tensor: every token, record and output offset
+# must be computed in 64 bits. T * H * 128 = (2^18 + 64) * 64 * 128 > 2^31; the
+# sampled heads include the last one, so the highest offsets are checked.
+@pytest.mark.parametrize("path", ["chunked", "recurrent"])
+def test_offsets_beyond_2g_elements(path):
+    device = dev()
+    w = kda_inputs.Workload("offsets_T262208_H64", B=1, T=2 ** 18 + 64, H=64, state='fp32')
+    assert w.T * w.H * 128 > 2 ** 31
+    say(f"{w.name}: {w.T} tokens x {w.H} heads, path={path} (inputs drawn on the device)")
+    x = kda_inputs.make_inputs_device(w, device)
+    out = torch.empty(1, w.T, w.H, 128, dtype=torch.bfloat16, device=device)
+    fin = torch.empty(1, w.H, 128, 128, dtype=torch.float32, device=device)
+    fn = kda.fwd if path == "chunked" else kda.fwd_recurrent
+    fn(x['q'], x['k'], x['v'], x['g'], x['beta'], x['scale'], out, x['A_log'], x['dt_bias'], x['lower_bound'],
+       initial_state=x['initial_state'], final_state=fin)
+    torch.cuda.synchronize()
+    heads = [0, w.H - 1]
+    cpu = {n: x[n][:, :, heads].contiguous().cpu() for n in ('q', 'k', 'v', 'g', 'beta')}
+    ro, rf = kda_oracle(cpu['q'], cpu['k'], cpu['v'], cpu['g'], cpu['beta'], x['scale'],
+                        x['A_log'][heads].cpu(), x['dt_bias'][heads].cpu(), x['lower_bound'],
+                        initial_state=x['initial_state'][:, heads].contiguous().cpu())
+    o = out[:, :, heads].float().double().cpu().numpy().reshape(w.T, len(heads), 128)
+    f = fin[:, heads].double().cpu().numpy()
+    del x, out
+    check(o, f, ro, rf, 'fp32', f"{w.name}/{path}")
