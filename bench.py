@@ -199,6 +199,9 @@ def main():
            "kda_intra_kernel": (IN_BYTES_PER_TOKEN_HEAD * tokens * H, rec_bytes),
            "kda_chain_kernel": (OUT_BYTES_PER_TOKEN_HEAD * tokens * H + state_in + state_out, rec_bytes)}
     kernels = {}
+    if args.path == "recurrent":   # one kernel per call: its time is the call's, on the same stream
+        per_kernel = {"kda_recurrent_kernel": (call_ms * args.steps, args.steps)}
+        alg["kda_recurrent_kernel"] = (alg_bytes, 0)
     for name, (tot_ms, launches) in per_kernel.items():
         if launches == 0:
             continue
@@ -230,10 +233,6 @@ def main():
                            "unit": "GB/s", "frac": kd["alg_GBps"] / HBM_PEAK_GBS,
                            "traffic": recorded_traffic(w.name, dom) if safe else None,
                            "alg_bytes_per_launch": kd["alg_bytes"], "avg_launch_ms": kd["avg_ms"]}
-    else:
-        res["roofline"] = {"kernel": "kda_recurrent_kernel (whole call)", "bound": "hbm", "achieved": achieved,
-                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                           "alg_bytes_per_launch": alg_bytes, "avg_launch_ms": call_ms}
     res["path"] = {"achieved_GBps": achieved, "frac_hbm": achieved / HBM_PEAK_GBS, "alg_bytes_per_call": alg_bytes,
                    "call_ms": call_ms, "mfma_tflops": flops / (call_ms * 1e-3) / 1e12,
                    "frac_mfma_bf16": flops / (call_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}

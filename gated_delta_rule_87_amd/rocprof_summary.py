@@ -11,7 +11,7 @@ Inputs are the directories rocprofv3 wrote with --output-format csv:
                  device copy): each counter's reading for a known byte count gives
                  its scale factor (bytes per counted KiB)
   --sq           --pmc runs of SQ_* counters
-Writes one <kernel>__<workload>.md per kernel of the kda_fwd call, the
+Writes one <kernel>__<workload>.md per kernel of the profiled call, the
 copy_calibration__1GiB.md table, and merges the per-launch HBM bytes into
 traffic.json, keyed by workload and by the hash of the kernel sources (bench.py
 reports a measured "traffic" only while that hash matches).
@@ -25,7 +25,7 @@ import os
 import statistics
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-KERNELS = ("kda_sched_kernel", "kda_intra_kernel", "kda_chain_kernel")
+KERNELS = ("kda_sched_kernel", "kda_intra_kernel", "kda_chain_kernel", "kda_recurrent_kernel")
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 GIB = 1 << 30
 
@@ -143,8 +143,10 @@ def main():
             if tot is not None:
                 fh.write(f"| total | | | {tot:.4g} |\n")
             if k in alg:
-                fh.write(f"\nAlgorithmic bytes of this kernel: {alg[k]['alg_bytes']:.4g}; "
-                         f"bytes the design moves (with the per-chunk records): {alg[k]['design_bytes']:.4g}.\n")
+                fh.write(f"\nAlgorithmic bytes of this kernel: {alg[k]['alg_bytes']:.4g}")
+                if alg[k]['design_bytes'] != alg[k]['alg_bytes']:
+                    fh.write(f"; bytes the design moves (with the per-chunk records): {alg[k]['design_bytes']:.4g}")
+                fh.write(".\n")
             rows = sorted((c, v) for (kk, c), v in sq.items() if kk == k)
             if rows:
                 fh.write("\n## SQ counters (mean per launch)\n\n| counter | value |\n|---|---|\n")
