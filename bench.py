@@ -30,7 +30,13 @@ fp32 final state). Prints ONE JSON line.
               design moves (including the per-chunk records written by the
               intra kernel and read back by the chain kernel)
   cpu_baseline the fp64 CPU oracle timed on the host cores over the same
-              workload (bounded: see "sample")
+              workload (bounded: see "sample"), with a one-thread figure
+
+Timing: W warm-up steps, then K timed steps between HIP events on the launch
+stream; the steps alternate between two input sets (distinct tensors, the
+second drawn with the next seed) so that no step finds its inputs in the
+last-level cache from the step before. "path" also reports the median and the
+minimum per-call time.
 """
 import argparse
 import json
@@ -103,6 +109,16 @@ def cpu_threads():
         return min(16, os.cpu_count() or 1)
 
 
+def host_cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,6 +152,9 @@ def main():
     w = kda_inputs.workload(args.workload)
     d = kda_inputs.make_inputs(w)
     x = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    w2 = kda_inputs.Workload(**{**w.__dict__, "seed": w.seed + 1})
+    x2 = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in kda_inputs.make_inputs(w2).items()}
+    sets = [x, x2]
     B, T, H = w.B, w.T, w.H
     tokens = B * T
     nseq = w.n_seqs
@@ -148,8 +167,11 @@ def main():
     ws = torch.empty(max(1, kda.workspace_size(B, T, H, N)), dtype=torch.uint8, device=dev)
 
     safe = args.gate == "safe"
+    nstep = [0]
 
     def step():
+        x = sets[nstep[0] & 1]
+        nstep[0] += 1
         if args.path == "chunked":
             kda.fwd(x['q'], x['k'], x['v'], x['g'], x['beta'], x['scale'], out, x['A_log'], x['dt_bias'],
                     x['lower_bound'], initial_state=x['initial_state'], final_state=fin,
@@ -234,7 +256,8 @@ def main():
                            "traffic": recorded_traffic(w.name, dom) if safe else None,
                            "alg_bytes_per_launch": kd["alg_bytes"], "avg_launch_ms": kd["avg_ms"]}
     res["path"] = {"achieved_GBps": achieved, "frac_hbm": achieved / HBM_PEAK_GBS, "alg_bytes_per_call": alg_bytes,
-                   "call_ms": call_ms, "mfma_tflops": flops / (call_ms * 1e-3) / 1e12,
+                   "call_ms": call_ms, "call_ms_median": sorted(per_call_ms)[len(per_call_ms) // 2],
+                   "call_ms_min": min(per_call_ms), "input_sets": 2, "mfma_tflops": flops / (call_ms * 1e-3) / 1e12,
                    "frac_mfma_bf16": flops / (call_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
     res["kernels"] = kernels
     res["wall_s_timed"] = t_wall
@@ -249,6 +272,12 @@ def main():
                    want_final=True, nthreads=nthr, safe_gate=safe)
         dt = time.perf_counter() - t
         chains = nseq * H
+        # one thread on one head, scaled to the whole workload
+        t1 = time.perf_counter()
+        kda_oracle(d['q'], d['k'], d['v'], d['g'], d['beta'], d['scale'], d['A_log'], d['dt_bias'],
+                   d['lower_bound'], initial_state=d['initial_state'], cu_seqlens=d['cu_seqlens'],
+                   heads=[0], want_final=True, nthreads=1, safe_gate=safe)
+        dt1 = (time.perf_counter() - t1) * H
         res["cpu_baseline"] = {
             "value": tokens / dt,
             "unit": "tokens/s",
@@ -256,6 +285,9 @@ def main():
             "kind": "oracle",
             "sample": f"whole workload ({tokens} tokens x {H} heads, fp64, {min(nthr, chains)} OpenMP "
                       f"threads over {chains} independent chains), {dt:.2f} s",
+            "one_thread_value": tokens / dt1,
+            "one_thread_sample": f"head 0 of the same workload on one thread, {dt1 / H:.2f} s, scaled to {H} heads",
+            "host": host_cpu_model(),
         }
         res["gpu_over_cpu"] = res["value"] / res["cpu_baseline"]["value"]
     print(json.dumps(res), flush=True)
