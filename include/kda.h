@@ -109,16 +109,16 @@ size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N);
 /*
  * kda_fwd -- chunked KDA prefill forward (64-token chunks).
  *
- *   q, k, g      bf16 [B, T, H, K]   query, key, gate before activation
+ *   q, k, g      bf16 [B, T, H, K]   query, key, raw gate input (activated inside)
  *   v            bf16 [B, T, H, V]   value
  *   beta         bf16 [B, T, H]      beta logits (sigmoid applied inside)
  *   scale        float               read-out scaling factor (finite)
  *   out          bf16 [B, T, H, V]   OUTPUT, written in place; every element
  *                                    is written, none is read (no need to
  *                                    pre-zero it)
- *   A_log        fp32 [H]            log-gate parameter
- *   dt_bias      fp32 [H, K]         gate bias
- *   lower_bound  float in [-5, 0]    gate lower bound
+ *   A_log        fp32 [H]            log of each head's gate rate
+ *   dt_bias      fp32 [H, K]         per-channel offset added to g
+ *   lower_bound  float in [-5, 0]    most negative value the gate can take
  *   initial_state, initial_dtype     NULL/KDA_STATE_NONE (zeros) or
  *                                    [B|N, H, V, K] bf16/fp32
  *   final_state, final_dtype         NULL/KDA_STATE_NONE (not written) or

@@ -24,8 +24,8 @@
  *   Parameter roles, shapes and dtypes follow the "Kernel API" table of the
  *   FlashKDA README digest (aiwatch.icu page): q, k, g [B,T,H,K] bf16,
  *   v [B,T,H,V] bf16, beta [B,T,H] bf16 logits with the sigmoid applied
- *   inside, A_log fp32 [H] "log-gate parameter", dt_bias fp32 [H,K] "gate
- *   bias", lower_bound "gate lower bound" in [-5, 0], state [B|N,H,V,K],
+ *   inside, A_log fp32 [H] (log of the gate rate), dt_bias fp32 [H,K] (an
+ *   offset added to g), lower_bound in [-5, 0] (the gate's floor), state [B|N,H,V,K],
  *   cu_seqlens int64 [N+1] with B = 1 and T the packed total length; without
  *   cu_seqlens every batch row is an independent sequence.
  *
