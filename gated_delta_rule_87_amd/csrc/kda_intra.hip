@@ -76,12 +76,18 @@ __device__ __forceinline__ u32x4 mul_f16x8(u32x4 a, u32x4 b) {   // packed fp16 
 __device__ __forceinline__ u32x2 pk4_f16(f32x4 v) { return u32x2{pack_f16x2(v.x, v.y), pack_f16x2(v.z, v.w)}; }
 __device__ __forceinline__ u32x2 pk4_bf16(f32x4 v) { return u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)}; }
 
-// channels chan(s, 0..7, gq) = 32s + {4gq..4gq+3, 16+4gq..16+4gq+3} of one token row
+// channels chan(s, 0..7, gq) = 32s + {4gq..4gq+3, 16+4gq..16+4gq+3} of one token row.
+// One 16-byte load per lane: lane group gq reads the 8 channels 32s + 8c.. with
+// c = (0, 2, 1, 3)[gq], so lane groups (0, 1) hold channels 0-7 and 16-23 and (2, 3)
+// hold 8-15 and 24-31; one cross-row swap per register pair then gives even groups
+// their partner's first four channels and odd groups their partner's last four.
 __device__ __forceinline__ u32x4 load_row8(const uint16_t* row, int s, int gq, bool valid) {
   if (!valid) return u32x4{0u, 0u, 0u, 0u};
-  const u32x2 a = *reinterpret_cast<const u32x2*>(row + 32 * s + 4 * gq);
-  const u32x2 b = *reinterpret_cast<const u32x2*>(row + 32 * s + 16 + 4 * gq);
-  return u32x4{a.x, a.y, b.x, b.y};
+  const int c = ((gq & 1) << 1) | (gq >> 1);
+  const u32x4 x = *reinterpret_cast<const u32x4*>(row + 32 * s + 8 * c);
+  const auto a = __builtin_amdgcn_permlane16_swap(x.x, x.z, false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(x.y, x.w, false, false);
+  return u32x4{a[0], b[0], a[1], b[1]};
 }
 __device__ __forceinline__ void ld8f(const float* p, float* f) {   // p -> channels +0..3 and +16..19
   const f32x4 a = *reinterpret_cast<const f32x4*>(p);
