@@ -366,3 +366,26 @@ def test_offsets_beyond_2g_elements(path):
     f = fin[:, heads].double().cpu().numpy()
     del x, out
     check(o, f, ro, rf, 'fp32', f"{w.name}/{path}")
+
+
+# ---------------------------------------------------------------------------
+# power-of-two scaling of v and the initial state: the forward is linear in (v, S0),
+# and every internal rescaling in the kernels (the U~ column scales, the state-row and
+# U-column scales of the chain) is a power of two, so out and final_state must scale
+# by exactly the same power of two, bit for bit
+@pytest.mark.parametrize("path", ["chunked", "recurrent"])
+@pytest.mark.parametrize("state", ["fp32", "bf16"])
+def test_power_of_two_scaling_is_exact(state, path):
+    device = dev()
+    w = kda_inputs.custom(lengths=[150, 64, 1, 77], H=2, state=state, final=state)
+    d = kda_inputs.make_inputs(w)
+    ref_o, ref_f = run(d, w, path)
+    for k in (-10, 16):
+        say(f"scale v and initial state by 2^{k}, state={state}, path={path}")
+        ds = dict(d)
+        ds['v'] = (d['v'].float() * 2.0 ** k).to(torch.bfloat16)
+        ds['initial_state'] = (d['initial_state'].float() * 2.0 ** k).to(d['initial_state'].dtype)
+        assert torch.equal(ds['v'].float(), d['v'].float() * 2.0 ** k)   # the scaling itself is exact
+        o, f = run(ds, w, path)
+        assert np.array_equal(o, ref_o * 2.0 ** k), f"out does not scale exactly by 2^{k}"
+        assert np.array_equal(f, ref_f * 2.0 ** k), f"final state does not scale exactly by 2^{k}"
