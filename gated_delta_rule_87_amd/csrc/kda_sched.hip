@@ -28,7 +28,9 @@ __global__ __launch_bounds__(SCHED_THREADS) void kda_sched_kernel(const int64_t*
                                                                   int32_t* seq_order) {
   __shared__ int32_t warp_sums[SCHED_THREADS / 64];
   __shared__ uint64_t keys[SORT_MAX];
+  __shared__ int2 s_tab[SORT_MAX], s_span[SORT_MAX];   // LDS copies of the tables (N <= SORT_MAX)
   __shared__ int32_t carry_s;
+  const bool in_lds = N <= SORT_MAX;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   if (tid == 0) carry_s = 0;
   __syncthreads();
@@ -63,6 +65,10 @@ __global__ __launch_bounds__(SCHED_THREADS) void kda_sched_kernel(const int64_t*
       const int32_t cnt = nc < max_chunks - f ? nc : max_chunks - f;
       seq_tab[n] = make_int2(f, cnt);
       seq_span[n] = make_int2(s, len);
+      if (in_lds) {
+        s_tab[n] = make_int2(f, cnt);
+        s_span[n] = make_int2(s, len);
+      }
     }
     __syncthreads();
     if (tid == SCHED_THREADS - 1) carry_s = carry + woff + x;
@@ -71,12 +77,15 @@ __global__ __launch_bounds__(SCHED_THREADS) void kda_sched_kernel(const int64_t*
   __threadfence_block();
   __syncthreads();
 
-  // pass 2: every chunk slot finds its sequence by binary search over seq_tab
+  // pass 2: every chunk slot finds its sequence by binary search over the table
+  // (in LDS up to SORT_MAX sequences, else the global copy written above)
+  auto tab = [&](int n) { return in_lds ? s_tab[n] : seq_tab[n]; };
+  auto span = [&](int n) { return in_lds ? s_span[n] : seq_span[n]; };
   for (int i = tid; i < max_chunks; i += SCHED_THREADS) {
     int lo = 0, hi = N - 1, found = -1;
-    while (lo <= hi) {   // last n with seq_tab[n].x <= i
+    while (lo <= hi) {   // last n with tab(n).x <= i
       const int mid = (lo + hi) >> 1;
-      if (seq_tab[mid].x <= i) {
+      if (tab(mid).x <= i) {
         found = mid;
         lo = mid + 1;
       } else {
@@ -85,10 +94,10 @@ __global__ __launch_bounds__(SCHED_THREADS) void kda_sched_kernel(const int64_t*
     }
     int2 e = make_int2(0, 0);
     if (found >= 0) {
-      const int2 st = seq_tab[found];
+      const int2 st = tab(found);
       const int jj = i - st.x;
       if (jj < st.y) {
-        const int2 sp = seq_span[found];
+        const int2 sp = span(found);
         const int32_t rem = sp.y - jj * CH;
         e = make_int2(sp.x + jj * CH, rem < CH ? rem : CH);
       }
@@ -105,7 +114,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void kda_sched_kernel(const int64_t*
   int np = 1;
   while (np < N) np <<= 1;
   for (int i = tid; i < np; i += SCHED_THREADS)
-    keys[i] = i < N ? ((uint64_t)(uint32_t)(0x7fffffff - seq_tab[i].y) << 32) | (uint32_t)i : ~0ull;
+    keys[i] = i < N ? ((uint64_t)(uint32_t)(0x7fffffff - s_tab[i].y) << 32) | (uint32_t)i : ~0ull;
   __syncthreads();
   for (int k = 2; k <= np; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
