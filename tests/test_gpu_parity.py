@@ -389,3 +389,18 @@ def test_power_of_two_scaling_is_exact(state, path):
         o, f = run(ds, w, path)
         assert np.array_equal(o, ref_o * 2.0 ** k), f"out does not scale exactly by 2^{k}"
         assert np.array_equal(f, ref_f * 2.0 ** k), f"final state does not scale exactly by 2^{k}"
+
+
+@pytest.mark.parametrize("path", ["chunked", "recurrent"])
+def test_scale_zero_and_sign(path):
+    """scale only multiplies the read-out: scale = 0 gives out == 0 exactly, -scale gives
+    -out bit for bit, and the final state does not depend on it."""
+    w = kda_inputs.custom(lengths=[100, 3, 64], H=2, state='fp32')
+    d = kda_inputs.make_inputs(w)
+    say(f"scale 0 / sign, path={path}")
+    o, f = run(d, w, path)
+    o0, f0 = run(dict(d, scale=0.0), w, path)
+    on, fn = run(dict(d, scale=-d['scale']), w, path)
+    assert np.all(o0 == 0.0), "scale = 0 must give a zero output"
+    assert np.array_equal(on, -o), "negating scale must negate out exactly"
+    assert np.array_equal(f0, f) and np.array_equal(fn, f), "final state must not depend on scale"
