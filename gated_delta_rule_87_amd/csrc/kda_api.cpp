@@ -31,10 +31,40 @@ inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
   int64_t max_chunks = 0;
-  size_t rec = 0, seq_tab = 0, chunk_tab = 0, seq_span = 0, seq_order = 0, total = 0;
+  int64_t nseg = 1;   // segments per row of the segment-parallel state chain (1: plain chain)
+  size_t rec = 0, seq_tab = 0, chunk_tab = 0, seq_span = 0, seq_order = 0, maps = 0, seg_init = 0, total = 0;
 };
 
-// Workspace regions: chunk records | seq_tab | chunk_tab | seq_span | seq_order.
+// Segments per row for the state chain of fixed-length inputs. The plain chain runs
+// one workgroup per (row, head, pair of 16-wide value tiles) through all nc chunks of
+// a row, one workgroup per compute unit, so with few (row, head) chains most of the
+// GPU idles. Cutting each row into s segments costs a maps pass over twice the value
+// rows, a scan of s steps and an outputs pass, each pass over nc / s chunks. Cost in
+// chunk steps, for 256 compute units:
+//   plain      nc * ceil(BH * 4 / 256)
+//   segmented  (nc / s) * (ceil(BH * s * 8 / 256) + ceil(BH * s * 4 / 256)) + 2 s
+// The smallest-cost power of two s with segments of at least 8 chunks is taken when it
+// saves at least 15%.
+int64_t chain_segments(int64_t B, int64_t nc, int64_t H) {
+  constexpr int64_t CUS = 256;
+  auto waves = [](int64_t wgs) { return (wgs + CUS - 1) / CUS; };
+  const int64_t BH = B * H;
+  const double plain = (double)nc * (double)waves(BH * 4);
+  int64_t best = 1;
+  double best_cost = plain;
+  for (int64_t s = 2; nc >= 8 * s && s <= 64; s *= 2) {
+    const int64_t sc = (nc + s - 1) / s;
+    const double cost = (double)sc * (double)(waves(BH * s * 8) + waves(BH * s * 4)) + 2.0 * (double)s;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  return best_cost <= 0.85 * plain ? best : 1;
+}
+
+// Workspace regions: chunk records | seq_tab | chunk_tab | seq_span | seq_order |
+// segment maps | segment initial states (the last two only with a segmented chain).
 bool make_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool varlen, Layout& L) {
   if (B < 1 || T < 0 || H < 1 || N < 0) return false;
   if (varlen) {
@@ -55,6 +85,12 @@ bool make_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool varlen, Layout
   off = align_up(off + (varlen ? (size_t)N * sizeof(int2) : 0));
   L.seq_order = off;
   off = align_up(off + (varlen ? (size_t)N * sizeof(int32_t) : 0));
+  L.nseg = varlen ? 1 : chain_segments(B, (T + kda::CH - 1) / kda::CH, H);
+  const size_t segs = L.nseg > 1 ? (size_t)(B * L.nseg * H) : 0;
+  L.maps = off;
+  off = align_up(off + segs * 2 * kda::VD * kda::KD * sizeof(float));
+  L.seg_init = off;
+  off = align_up(off + segs * kda::VD * kda::KD * sizeof(float));
   L.total = off;
   return true;
 }
@@ -231,6 +267,18 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
   p.map.max_chunks = (int32_t)L.max_chunks;
   p.map.nseq = (int32_t)(varlen ? N : B);
   p.map.nc_row = (int32_t)((T + kda::CH - 1) / kda::CH);
+  // segment-parallel chain: the layout's segment count, or fewer with KDA_CHAIN_SEGMENTS
+  int64_t nseg = L.nseg;
+  if (const char* e = std::getenv("KDA_CHAIN_SEGMENTS")) {
+    const long v = std::strtol(e, nullptr, 10);
+    if (v >= 1 && v < nseg) nseg = v;
+  }
+  if (nseg > 1) {
+    p.seg.nseg = (int32_t)nseg;
+    p.seg.seg_chunks = (int32_t)((p.map.nc_row + nseg - 1) / nseg);
+    p.seg.maps = reinterpret_cast<float*>(ws + L.maps);
+    p.seg.seg_init = reinterpret_cast<float*>(ws + L.seg_init);
+  }
   if (varlen) {
     p.map.seq_tab = reinterpret_cast<const int2*>(ws + L.seq_tab);
     p.map.chunk_tab = reinterpret_cast<const int2*>(ws + L.chunk_tab);
@@ -238,9 +286,9 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
     p.map.seq_order = reinterpret_cast<const int32_t*>(ws + L.seq_order);
   }
   if (env_flag("KDA_LOG"))
-    std::fprintf(stderr, "[kda] fwd B=%lld T=%lld H=%lld N=%lld chunks=%lld workspace=%zu varlen=%d\n",
+    std::fprintf(stderr, "[kda] fwd B=%lld T=%lld H=%lld N=%lld chunks=%lld workspace=%zu varlen=%d segments=%lld\n",
                  (long long)B, (long long)T, (long long)H, (long long)N, (long long)L.max_chunks, L.total,
-                 (int)varlen);
+                 (int)varlen, (long long)nseg);
 
   CallTimer tm(st);
   hipError_t e = tm.mark(0);
@@ -257,7 +305,14 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
     tm.launched(1);
   }
   if (e == hipSuccess) e = tm.mark(2);
-  if (e == hipSuccess) {
+  if (e == hipSuccess && nseg > 1) {   // segment maps, their composition, then the outputs
+    p.seg.mode = kda::CHAIN_MAPS;
+    e = kda::launch_chain(p, st);
+    if (e == hipSuccess) e = kda::launch_scan(p, (int32_t)B, st);
+    p.seg.mode = kda::CHAIN_OUTPUTS;
+    if (e == hipSuccess) e = kda::launch_chain(p, st);
+    tm.launched(2);
+  } else if (e == hipSuccess) {
     e = kda::launch_chain(p, st);
     tm.launched(2);
   }

@@ -119,7 +119,9 @@ __global__ __launch_bounds__((2 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
   __shared__ ChainXchg<NW> xc;
 
   const int H = p.H;
-  const int NH = p.map.nseq * H;
+  const int mode = p.seg.mode;
+  // segment modes: "sequence" n' = row * nseg + segment
+  const int NH = (mode == CHAIN_FULL ? p.map.nseq : p.map.nseq * p.seg.nseg) * H;
   // workgroups of one (sequence, head) share blockIdx % 8, i.e. one XCD and its L2
   const int id = blockIdx.x;
   const int xcd = id & 7, rest = id >> 3;
@@ -128,13 +130,19 @@ __global__ __launch_bounds__((2 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
   if (nh >= NH) return;   // uniform over the block
   // varlen: walk the sequences longest first, so long chains do not start last
   const int rank = nh / H, h = nh - rank * H;
-  const int n = p.map.seq_order ? __builtin_amdgcn_readfirstlane(p.map.seq_order[rank]) : rank;
+  const int n = (mode == CHAIN_FULL && p.map.seq_order) ? __builtin_amdgcn_readfirstlane(p.map.seq_order[rank]) : rank;
 
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, uniform
   const int l = threadIdx.x & 63, lt = l & 15, gq = l >> 4;
 
   int c0, nc, tok0, len;
-  if (p.map.seq_tab) {
+  if (mode != CHAIN_FULL) {   // one segment of a fixed-length row
+    const int row = n / p.seg.nseg, cs = (n - row * p.seg.nseg) * p.seg.seg_chunks;
+    c0 = row * p.map.nc_row + cs;
+    nc = max(0, min(p.seg.seg_chunks, p.map.nc_row - cs));
+    tok0 = row * p.map.T + cs * CH;
+    len = max(0, min(p.seg.seg_chunks * CH, p.map.T - cs * CH));
+  } else if (p.map.seq_tab) {
     const int2 e = p.map.seq_tab[n];
     const int2 sp = p.map.seq_span[n];
     c0 = __builtin_amdgcn_readfirstlane(e.x);
@@ -173,9 +181,10 @@ __global__ __launch_bounds__((2 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDSPTR(&d.ut[s][2 * hh][0]), 16, lane16,
-                                                   OFF_UT + (vg * NW + s) * 2048 + hh * FRAG, 0, 0);
+                                                   OFF_UT + ((vg * NW + s) & 7) * 2048 + hh * FRAG, 0, 0);
       }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDSPTR(&d.usc[0]), 16, lane16, OFF_USC + NW * 256 * vg, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDSPTR(&d.usc[0]), 16, lane16,
+                                               OFF_USC + NW * 256 * (vg % (VD / (16 * NW))), 0, 0);
     };
     auto load_part2 = [&](int j) {
       const __amdgpu_buffer_rsrc_t rs = rsrc(j);
@@ -226,7 +235,20 @@ __global__ __launch_bounds__((2 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
     // state slice, D layout of S^T: S[mt][j] = S[16 vt + lt][16 mt + 4 gq + j]
     f32x4 S[8];
     const size_t st_off = ((size_t)(n * H + h) * VD + 16 * vt + lt) * KD;
-    if (p.init_dtype == 2) {
+    // maps pass: tiles 0-7 are the value rows from a zero state (R), tiles 8-15 the rows
+    // of the identity run without U~ (P); outputs pass: the scanned segment state
+    const bool ptile = mode == CHAIN_MAPS && vt >= 8;
+    if (mode == CHAIN_MAPS) {
+      const int r = 16 * (vt - 8) + lt;   // identity row of a P tile
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) S[mt][jj] = (ptile && 16 * mt + 4 * gq + jj == r) ? 1.0f : 0.0f;
+    } else if (mode == CHAIN_OUTPUTS) {
+      const float* src = p.seg.seg_init + st_off;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) S[mt] = *reinterpret_cast<const f32x4*>(src + 16 * mt + 4 * gq);
+    } else if (p.init_dtype == 2) {
       const float* src = static_cast<const float*>(p.init_state) + st_off;
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) S[mt] = *reinterpret_cast<const f32x4*>(src + 16 * mt + 4 * gq);
@@ -272,7 +294,8 @@ __global__ __launch_bounds__((2 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
         for (int q = 0; q < 4; ++q) acc = mfma_f16(P1.wneg[mt * 4 + q][l], sf[q], acc);
         const u32x2 uh = P1.ut[s][mt][l];
         const f32x2 u01 = unpack_f16x2(uh.x), u23 = unpack_f16x2(uh.y);
-        U[mt] = f32x4{u01.x, u01.y, u23.x, u23.y} * P1.usc[s * 64 + mt * 16 + lt] + acc * iS;
+        const f32x4 ut = ptile ? f32x4{0, 0, 0, 0} : f32x4{u01.x, u01.y, u23.x, u23.y} * P1.usc[s * 64 + mt * 16 + lt];
+        U[mt] = ut + acc * iS;
       }
       float sU, iU;
       pow2_scale(row_absmax(U, 4), sU, iU);
@@ -298,7 +321,13 @@ __global__ __launch_bounds__((2 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
       publish_state();
     }
 
-    if (p.final_dtype == 2) {
+    if (mode == CHAIN_MAPS) {
+      float* dst = p.seg.maps + ((size_t)(n * H + h) * (2 * VD) + 16 * vt + lt) * KD;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(dst + 16 * mt + 4 * gq) = S[mt];
+    } else if (mode == CHAIN_OUTPUTS) {
+      // the scan writes final_state
+    } else if (p.final_dtype == 2) {
       float* dst = static_cast<float*>(p.final_state) + st_off;
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(dst + 16 * mt + 4 * gq) = S[mt];
@@ -316,6 +345,13 @@ __global__ __launch_bounds__((2 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
   // O^T = scale (S0 Qg^T + U^T Aqk^T)   D layout: lane <-> token 16 nt + lt, registers <-> v.
   // Register jj of lane group gq belongs to value row 4 gq + jj of the tile.
   const float scale = p.scale;
+  if (mode == CHAIN_MAPS) {   // no outputs: keep the two barriers of every chunk step
+    for (int j = 0; j < nc; ++j) {
+      lds_barrier();   // (A)
+      lds_barrier();   // (B)
+    }
+    return;
+  }
   for (int j = 0; j < nc; ++j) {
     const ChainPart1<NW>& P1 = r1[j & 1];
     const ChainPart2<NW>& P2 = r2[j & 1];
@@ -362,8 +398,8 @@ static_assert(OFF_QG == 16 * FRAG && OFF_KP == 32 * FRAG && OFF_AQK == 48 * FRAG
               "shared fragments must be contiguous at the record start");
 
 template <int NW>
-hipError_t launch_chain_nw(const FwdParams& p, int NH, hipStream_t stream) {
-  const int nvg = VD / (16 * NW);
+hipError_t launch_chain_nw(const FwdParams& p, int NH, int rows, hipStream_t stream) {
+  const int nvg = rows / (16 * NW);
   const int64_t blocks = (int64_t)((NH + 7) / 8) * 8 * nvg;
   hipLaunchKernelGGL((kda_chain_kernel<NW>), dim3((unsigned)blocks), dim3((2 * NW + 1) * 64), 0, stream, p, nvg);
   return hipGetLastError();
@@ -375,7 +411,8 @@ hipError_t launch_chain_nw(const FwdParams& p, int NH, hipStream_t stream) {
 // compute units idle (more, shorter workgroups); four once there are enough
 // chains, which halves how often each record's shared fragments are fetched.
 hipError_t launch_chain(const FwdParams& p, hipStream_t stream) {
-  const int NH = p.map.nseq * p.H;
+  const int NH = (p.seg.mode == CHAIN_FULL ? p.map.nseq : p.map.nseq * p.seg.nseg) * p.H;
+  const int rows = p.seg.mode == CHAIN_MAPS ? 2 * VD : VD;   // value rows, plus the P rows of the maps pass
   if (NH <= 0) return hipSuccess;
   static const int cus = [] {   // compute units of the device (thread-safe one-time query)
     int dev = 0, n = 0;
@@ -384,7 +421,8 @@ hipError_t launch_chain(const FwdParams& p, hipStream_t stream) {
       return n;
     return 256;
   }();
-  return (int64_t)NH * (VD / 32) <= cus ? launch_chain_nw<2>(p, NH, stream) : launch_chain_nw<4>(p, NH, stream);
+  return (int64_t)NH * (rows / 32) <= cus ? launch_chain_nw<2>(p, NH, rows, stream)
+                                          : launch_chain_nw<4>(p, NH, rows, stream);
 }
 
 }  // namespace kda

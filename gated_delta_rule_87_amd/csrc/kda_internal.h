@@ -23,6 +23,21 @@ struct ChunkMap {
   int32_t nseq;            // sequences (B or N)
 };
 
+// Segment-parallel state chain (fixed-length rows only). Each row's chunks are cut
+// into nseg segments of seg_chunks chunks. Every segment acts on the state as an
+// affine map S -> S P + R; the chain kernel computes (P, R) of all segments at once
+// (CHAIN_MAPS: R from a zero state, P by running the identity through the recurrence
+// without U~), the scan kernel composes them into each segment's initial state, and
+// the chain kernel then produces the outputs of all segments at once (CHAIN_OUTPUTS).
+enum ChainMode : int32_t { CHAIN_FULL = 0, CHAIN_MAPS = 1, CHAIN_OUTPUTS = 2 };
+struct ChainSeg {
+  int32_t nseg = 1;        // segments per row (1: the plain chain)
+  int32_t seg_chunks = 0;  // chunks per segment (the last one may be shorter)
+  int32_t mode = CHAIN_FULL;
+  float* maps = nullptr;      // [rows * nseg][H][256][128] fp32: rows 0-127 R, rows 128-255 P
+  float* seg_init = nullptr;  // [rows * nseg][H][128][128] fp32: each segment's initial state
+};
+
 struct FwdParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -42,6 +57,7 @@ struct FwdParams {
   uint32_t flags;          // KDA_FUSE_* bits (which input processing runs in the kernels), GATE_UNBOUNDED
   ChunkMap map;
   uint8_t* rec;            // chunk records: [max_chunks][H][REC_BYTES]
+  ChainSeg seg;
 };
 
 hipError_t launch_sched(const int64_t* cu_seqlens, int32_t N, int32_t T, int32_t max_chunks,
@@ -49,6 +65,7 @@ hipError_t launch_sched(const int64_t* cu_seqlens, int32_t N, int32_t T, int32_t
                         hipStream_t stream);
 hipError_t launch_intra(const FwdParams& p, hipStream_t stream);
 hipError_t launch_chain(const FwdParams& p, hipStream_t stream);
+hipError_t launch_scan(const FwdParams& p, int32_t rows, hipStream_t stream);
 hipError_t launch_recurrent(const FwdParams& p, const int64_t* cu_seqlens, hipStream_t stream);
 
 }  // namespace kda

@@ -66,7 +66,8 @@ def ragged_lengths(gen: torch.Generator, n: int, lo: int = 64, hi: int = 4096) -
 
 
 def workload(idx: int) -> Workload:
-    """The named workloads (by index): 0-4 prefill shapes, 5 a decode step."""
+    """The named workloads (by index): 0-4 prefill shapes, 5 a decode step, 6 the
+    prefill's per-GPU share under 8-way head (tensor) parallelism."""
     if idx == 0:
         return Workload("tiny_T256_H2", B=1, T=256, H=2)
     if idx == 1:
@@ -82,6 +83,8 @@ def workload(idx: int) -> Workload:
         return Workload("batched_B4_T32768_H64", B=4, T=32768, H=64, state='fp32')
     if idx == 5:   # one generation step: one token per sequence, state passed in and out
         return Workload("decode_N256_H64", B=1, T=256, H=64, lengths=[1] * 256, state='fp32')
+    if idx == 6:   # one GPU's share of the prefill when the 64 heads are split over 8 GPUs
+        return Workload("tp8_share_T8192_H8", B=1, T=8192, H=8)
     raise ValueError(idx)
 
 

@@ -192,3 +192,17 @@ def test_unbounded_gate_skips_lower_bound_check(recurrent):
         assert call_ex(7, recurrent, lb=lb) == EVALUE
         assert call_ex(7 | 8, recurrent, lb=lb, K=64) == ESHAPE
         assert call_ex(8, recurrent, lb=lb, A_log=None, dt_bias=None, K=64) == ESHAPE
+
+
+def test_workspace_size_with_segmented_chain():
+    """Few (row, head) chains on long rows: the workspace adds the segment maps (256 x 128
+    fp32 per segment and head) and the segment initial states (128 x 128 fp32)."""
+    rec = 76288
+    al = lambda x: (x + 255) // 256 * 256
+    nseg = 8   # 8 heads x 8192 tokens: the chain is cut into 8 segments of 16 chunks
+    m = 256 * 128 * 4
+    i = 128 * 128 * 4
+    assert kda.workspace_size(1, 8192, 8) == al(128 * 8 * rec) + al(nseg * 8 * m) + al(nseg * 8 * i)
+    # enough chains for the whole GPU, or varlen input: no segment buffers
+    assert kda.workspace_size(1, 8192, 64) == al(128 * 64 * rec)
+    assert kda.workspace_size(1, 8192, 8, 1) == al((128 + 1) * 8 * rec) + al(8) + al(129 * 8) + al(8) + al(4)

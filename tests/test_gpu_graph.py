@@ -109,3 +109,40 @@ def test_graph_replay_decode_loop():
         torch.cuda.synchronize()
         assert torch.equal(out, o_ref), f"step {t}: out differs from the eager step"
         assert torch.equal(state, ref_state), f"step {t}: state differs from the eager step"
+
+
+def test_graph_replay_segmented_chain():
+    """The segment-parallel chain (maps pass, scan, outputs pass) captured and replayed."""
+    device = dev()
+    w = kda_inputs.custom(B=1, T=4096, H=2, state='fp32', lower_bound=-0.05)
+    say("graph capture of kda_fwd with the segmented chain (T=4096, H=2), 3 replays")
+    x = _inputs(w, 0, device)
+    B, T, H = x['q'].shape[:3]
+    out = torch.empty(B, T, H, 128, dtype=torch.bfloat16, device=device)
+    fin = torch.empty(B, H, 128, 128, dtype=torch.float32, device=device)
+    ws = torch.empty(kda.workspace_size(B, T, H), dtype=torch.uint8, device=device)
+
+    def call(o, f):
+        kda.fwd(x['q'], x['k'], x['v'], x['g'], x['beta'], x['scale'], o, x['A_log'], x['dt_bias'],
+                x['lower_bound'], initial_state=x['initial_state'], final_state=f, workspace=ws)
+
+    side = torch.cuda.Stream(device)
+    side.wait_stream(torch.cuda.current_stream(device))
+    with torch.cuda.stream(side):
+        call(out, fin)
+    torch.cuda.current_stream(device).wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out, fin)
+    for rep, seed in enumerate([1, 2, 3]):
+        nx = _inputs(w, seed, device)
+        for n in ('q', 'k', 'v', 'g', 'beta', 'A_log', 'dt_bias', 'initial_state'):
+            x[n].copy_(nx[n])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        o_ref, f_ref = torch.empty_like(out), torch.empty_like(fin)
+        call(o_ref, f_ref)
+        torch.cuda.synchronize()
+        assert torch.equal(out, o_ref) and torch.equal(fin, f_ref), f"replay {rep} differs from the eager call"

@@ -404,3 +404,69 @@ def test_scale_zero_and_sign(path):
     assert np.all(o0 == 0.0), "scale = 0 must give a zero output"
     assert np.array_equal(on, -o), "negating scale must negate out exactly"
     assert np.array_equal(f0, f) and np.array_equal(fn, f), "final state must not depend on scale"
+
+
+# ---------------------------------------------------------------------------
+# segment-parallel state chain: with few (row, head) chains on long fixed-length rows
+# the chain is cut into segments (affine maps, a scan, then the outputs). Checked
+# against the oracle and against the plain chain (KDA_CHAIN_SEGMENTS=1) on the same
+# inputs; KDA_LOG shows which segment count ran.
+# Gates with long memory (lower_bound near 0): a segment's initial state then still
+# matters at its end, so the P maps and the scan are exercised (with lower_bound = -5 a
+# 512-token segment forgets its initial state entirely and P underflows to 0).
+SEG_SHAPES = [
+    (dict(B=1, T=4096, H=2, state='fp32', lower_bound=-0.01), 8),                     # 8 segments of 8 chunks
+    (dict(B=2, T=4000, H=2, state='bf16', final='bf16', lower_bound=-0.05), 4),       # ragged last chunk
+    (dict(B=1, T=4096, H=1, final=None, lower_bound=-0.3), 8),                        # stateless, no final state
+    (dict(B=1, T=4096, H=2, state='fp32', lower_bound=-5.0), 8),                      # short memory
+]
+
+
+@pytest.mark.parametrize("shape,nseg", SEG_SHAPES,
+                         ids=["T4096_H2_fp32_lb0.01", "B2_T4000_H2_bf16_lb0.05", "T4096_H1_nofinal_lb0.3",
+                              "T4096_H2_fp32_lb5"])
+def test_segmented_chain(shape, nseg, capfd, monkeypatch):
+    w = kda_inputs.custom(**shape)
+    say(f"segmented chain {shape}")
+    d = kda_inputs.make_inputs(w)
+    ro, rf = oracle_for(d)
+    monkeypatch.setenv("KDA_LOG", "1")
+    o, f = run(d, w)
+    assert f"segments={nseg}" in capfd.readouterr().err, "the segmented chain did not run"
+    check(o, f, ro, rf if w.final else None, w.final, f"segmented x{nseg}")
+    monkeypatch.setenv("KDA_CHAIN_SEGMENTS", "1")
+    o1, f1 = run(d, w)
+    assert "segments=1" in capfd.readouterr().err
+    check(o1, f1, ro, rf if w.final else None, w.final, "plain chain")
+    say(f"segmented vs plain: out max-abs {np.abs(o - o1).max():.3e}")
+
+
+def test_segmented_chain_unbounded_mild_gate(capfd, monkeypatch):
+    """The gate without the safe bound at a small rate (long memory), segmented chain."""
+    w = kda_inputs.custom(B=1, T=4096, H=2, state='fp32')
+    d = _unbounded_inputs(kda_inputs.make_inputs(w), "mild")
+    say("segmented chain, unbounded mild gate")
+    ro, rf = kda_oracle(d['q'], d['k'], d['v'], d['g'], d['beta'], d['scale'], d['A_log'], d['dt_bias'],
+                        d['lower_bound'], initial_state=d['initial_state'], safe_gate=False)
+    monkeypatch.setenv("KDA_LOG", "1")
+    device = dev()
+    x = to_dev(d, device)
+    out = torch.empty(1, w.T, 2, 128, dtype=torch.bfloat16, device=device)
+    fin = torch.empty(1, 2, 128, 128, dtype=torch.float32, device=device)
+    kda.fwd(x['q'], x['k'], x['v'], x['g'], x['beta'], x['scale'], out, x['A_log'], x['dt_bias'], x['lower_bound'],
+            initial_state=x['initial_state'], final_state=fin, safe_gate=False)
+    torch.cuda.synchronize()
+    assert "segments=8" in capfd.readouterr().err
+    check(out.float().double().cpu().numpy().reshape(w.T, 2, 128), fin.double().cpu().numpy(), ro, rf, 'fp32',
+          "segmented, unbounded mild gate")
+
+
+def test_segmented_chain_tp8_share_sampled():
+    """One GPU's share under 8-way head parallelism (T=8192, H=8), segmented chain, sampled heads."""
+    w = kda_inputs.workload(6)
+    heads = [0, 5, 7]
+    say(f"workload 6 {w.name} heads={heads}")
+    d = kda_inputs.make_inputs(w)
+    o, f = run(d, w)
+    ro, rf = oracle_for(d, heads=heads)
+    check(o, f, ro, rf, w.final, w.name, heads=heads)
