@@ -112,14 +112,14 @@ struct ChainXchg {               // state wave -> output wave operands of one ch
   float iU[NW][16];              // 1 / column scale of U
 };
 
-template <int NW>
+template <int NW, int MODE>
 __global__ __launch_bounds__((2 * NW + 1) * 64) void kda_chain_kernel(FwdParams p, int nvg) {
   __shared__ ChainPart1<NW> r1[2];
   __shared__ ChainPart2<NW> r2[2];
   __shared__ ChainXchg<NW> xc;
 
   const int H = p.H;
-  const int mode = p.seg.mode;
+  constexpr int mode = MODE;   // ChainMode, fixed per instantiation
   // segment modes: "sequence" n' = row * nseg + segment
   const int NH = (mode == CHAIN_FULL ? p.map.nseq : p.map.nseq * p.seg.nseg) * H;
   // workgroups of one (sequence, head) share blockIdx % 8, i.e. one XCD and its L2
@@ -401,7 +401,13 @@ template <int NW>
 hipError_t launch_chain_nw(const FwdParams& p, int NH, int rows, hipStream_t stream) {
   const int nvg = rows / (16 * NW);
   const int64_t blocks = (int64_t)((NH + 7) / 8) * 8 * nvg;
-  hipLaunchKernelGGL((kda_chain_kernel<NW>), dim3((unsigned)blocks), dim3((2 * NW + 1) * 64), 0, stream, p, nvg);
+  const dim3 grid((unsigned)blocks), block((2 * NW + 1) * 64);
+  if (p.seg.mode == CHAIN_MAPS)
+    hipLaunchKernelGGL((kda_chain_kernel<NW, CHAIN_MAPS>), grid, block, 0, stream, p, nvg);
+  else if (p.seg.mode == CHAIN_OUTPUTS)
+    hipLaunchKernelGGL((kda_chain_kernel<NW, CHAIN_OUTPUTS>), grid, block, 0, stream, p, nvg);
+  else
+    hipLaunchKernelGGL((kda_chain_kernel<NW, CHAIN_FULL>), grid, block, 0, stream, p, nvg);
   return hipGetLastError();
 }
 
