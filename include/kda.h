@@ -33,6 +33,10 @@
  *     access memory out of bounds (results are then unspecified). Setting the
  *     environment variable KDA_VALIDATE=1 makes kda_fwd synchronise the stream
  *     and check the contents on the host (KDA_ERR_VALUE if violated).
+ *   - Other environment variables: KDA_LOG=1 prints each kda_fwd call's sizes
+ *     and chain segment count to stderr; KDA_CHAIN_SEGMENTS=n caps the number
+ *     of segments of the segment-parallel state chain (see
+ *     kda_fwd_workspace_size; 1 keeps the plain chain).
  */
 #ifndef KDA_H
 #define KDA_H
@@ -102,7 +106,11 @@ enum kda_state_dtype {
  *   B, T, H: as for kda_fwd;  N: number of sequences when cu_seqlens is used,
  *   0 otherwise. Returns 0 for invalid sizes (B < 1, T < 0, H < 1, N < 0).
  * The workspace holds the per-chunk intermediates of the chunked (WY) form
- * (74.5 KiB per 64-token chunk and head) and the varlen chunk tables.
+ * (74.5 KiB per 64-token chunk and head) and the varlen chunk tables. For
+ * fixed-length rows with few (row, head) pairs it also holds the buffers of
+ * the segment-parallel state chain: each row's chunks are cut into s segments
+ * (s chosen from B, T and H), with 192 KiB per (row, segment, head) for the
+ * segments' affine maps and initial states.
  */
 size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N);
 
