@@ -35,7 +35,8 @@ struct Layout {
   size_t rec = 0, seq_tab = 0, chunk_tab = 0, seq_span = 0, seq_order = 0, maps = 0, seg_init = 0, total = 0;
 };
 
-// Segments per row for the state chain of fixed-length inputs. The plain chain runs
+// Segments per row (fixed length) or sequence (varlen, with nc the average chunk
+// count, as the lengths stay on the device) for the state chain. The plain chain runs
 // one workgroup per (row, head, pair of 16-wide value tiles) through all nc chunks of
 // a row, one workgroup per compute unit, so with few (row, head) chains most of the
 // GPU idles. Cutting each row into s segments costs a maps pass over twice the value
@@ -85,8 +86,9 @@ bool make_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool varlen, Layout
   off = align_up(off + (varlen ? (size_t)N * sizeof(int2) : 0));
   L.seq_order = off;
   off = align_up(off + (varlen ? (size_t)N * sizeof(int32_t) : 0));
-  L.nseg = varlen ? 1 : chain_segments(B, (T + kda::CH - 1) / kda::CH, H);
-  const size_t segs = L.nseg > 1 ? (size_t)(B * L.nseg * H) : 0;
+  const int64_t seqs = varlen ? N : B;
+  L.nseg = seqs > 0 ? chain_segments(seqs, varlen ? T / (kda::CH * N) : (T + kda::CH - 1) / kda::CH, H) : 1;
+  const size_t segs = L.nseg > 1 ? (size_t)(seqs * L.nseg * H) : 0;
   L.maps = off;
   off = align_up(off + segs * 2 * kda::VD * kda::KD * sizeof(float));
   L.seg_init = off;
@@ -275,7 +277,6 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
   }
   if (nseg > 1) {
     p.seg.nseg = (int32_t)nseg;
-    p.seg.seg_chunks = (int32_t)((p.map.nc_row + nseg - 1) / nseg);
     p.seg.maps = reinterpret_cast<float*>(ws + L.maps);
     p.seg.seg_init = reinterpret_cast<float*>(ws + L.seg_init);
   }
@@ -308,7 +309,7 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
   if (e == hipSuccess && nseg > 1) {   // segment maps, their composition, then the outputs
     p.seg.mode = kda::CHAIN_MAPS;
     e = kda::launch_chain(p, st);
-    if (e == hipSuccess) e = kda::launch_scan(p, (int32_t)B, st);
+    if (e == hipSuccess) e = kda::launch_scan(p, p.map.nseq, st);
     p.seg.mode = kda::CHAIN_OUTPUTS;
     if (e == hipSuccess) e = kda::launch_chain(p, st);
     tm.launched(2);

@@ -136,12 +136,27 @@ __global__ __launch_bounds__((2 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
   const int l = threadIdx.x & 63, lt = l & 15, gq = l >> 4;
 
   int c0, nc, tok0, len;
-  if (mode != CHAIN_FULL) {   // one segment of a fixed-length row
-    const int row = n / p.seg.nseg, cs = (n - row * p.seg.nseg) * p.seg.seg_chunks;
-    c0 = row * p.map.nc_row + cs;
-    nc = max(0, min(p.seg.seg_chunks, p.map.nc_row - cs));
-    tok0 = row * p.map.T + cs * CH;
-    len = max(0, min(p.seg.seg_chunks * CH, p.map.T - cs * CH));
+  if (mode != CHAIN_FULL) {   // one segment of a row (fixed length) or a sequence (varlen)
+    const int row = n / p.seg.nseg, sg = n - row * p.seg.nseg;
+    int first, count, t0, length;
+    if (p.map.seq_tab) {
+      const int2 e = p.map.seq_tab[row], sp = p.map.seq_span[row];
+      first = __builtin_amdgcn_readfirstlane(e.x);
+      count = __builtin_amdgcn_readfirstlane(e.y);
+      t0 = __builtin_amdgcn_readfirstlane(sp.x);
+      length = __builtin_amdgcn_readfirstlane(sp.y);
+    } else {
+      first = row * p.map.nc_row;
+      count = p.map.nc_row;
+      t0 = row * p.map.T;
+      length = p.map.T;
+    }
+    const int sc = (count + p.seg.nseg - 1) / p.seg.nseg;   // chunks per segment of this row
+    const int cs = sg * sc;
+    c0 = first + cs;
+    nc = max(0, min(sc, count - cs));
+    tok0 = t0 + cs * CH;
+    len = max(0, min(sc * CH, length - cs * CH));
   } else if (p.map.seq_tab) {
     const int2 e = p.map.seq_tab[n];
     const int2 sp = p.map.seq_span[n];

@@ -23,19 +23,18 @@ struct ChunkMap {
   int32_t nseq;            // sequences (B or N)
 };
 
-// Segment-parallel state chain (fixed-length rows only). Each row's chunks are cut
-// into nseg segments of seg_chunks chunks. Every segment acts on the state as an
+// Segment-parallel state chain. Each row's (fixed length) or sequence's (varlen)
+// chunks are cut into nseg segments of ceil(chunks / nseg). Every segment acts on the state as an
 // affine map S -> S P + R; the chain kernel computes (P, R) of all segments at once
 // (CHAIN_MAPS: R from a zero state, P by running the identity through the recurrence
 // without U~), the scan kernel composes them into each segment's initial state, and
 // the chain kernel then produces the outputs of all segments at once (CHAIN_OUTPUTS).
 enum ChainMode : int32_t { CHAIN_FULL = 0, CHAIN_MAPS = 1, CHAIN_OUTPUTS = 2 };
 struct ChainSeg {
-  int32_t nseg = 1;        // segments per row (1: the plain chain)
-  int32_t seg_chunks = 0;  // chunks per segment (the last one may be shorter)
+  int32_t nseg = 1;        // segments per row or sequence (1: the plain chain)
   int32_t mode = CHAIN_FULL;
-  float* maps = nullptr;      // [rows * nseg][H][256][128] fp32: rows 0-127 R, rows 128-255 P
-  float* seg_init = nullptr;  // [rows * nseg][H][128][128] fp32: each segment's initial state
+  float* maps = nullptr;      // [seqs * nseg][H][256][128] fp32: rows 0-127 R, rows 128-255 P
+  float* seg_init = nullptr;  // [seqs * nseg][H][128][128] fp32: each segment's initial state
 };
 
 struct FwdParams {

@@ -106,11 +106,11 @@ enum kda_state_dtype {
  *   B, T, H: as for kda_fwd;  N: number of sequences when cu_seqlens is used,
  *   0 otherwise. Returns 0 for invalid sizes (B < 1, T < 0, H < 1, N < 0).
  * The workspace holds the per-chunk intermediates of the chunked (WY) form
- * (74.5 KiB per 64-token chunk and head) and the varlen chunk tables. For
- * fixed-length rows with few (row, head) pairs it also holds the buffers of
- * the segment-parallel state chain: each row's chunks are cut into s segments
- * (s chosen from B, T and H), with 192 KiB per (row, segment, head) for the
- * segments' affine maps and initial states.
+ * (74.5 KiB per 64-token chunk and head) and the varlen chunk tables. With few
+ * (row or sequence, head) pairs on long rows it also holds the buffers of the
+ * segment-parallel state chain: each row's or sequence's chunks are cut into s
+ * segments (s chosen from B or N, T and H), with 192 KiB per (row or sequence,
+ * segment, head) for the segments' affine maps and initial states.
  */
 size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N);
 

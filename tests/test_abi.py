@@ -203,6 +203,15 @@ def test_workspace_size_with_segmented_chain():
     m = 256 * 128 * 4
     i = 128 * 128 * 4
     assert kda.workspace_size(1, 8192, 8) == al(128 * 8 * rec) + al(nseg * 8 * m) + al(nseg * 8 * i)
-    # enough chains for the whole GPU, or varlen input: no segment buffers
+    # enough chains for the whole GPU: no segment buffers
     assert kda.workspace_size(1, 8192, 64) == al(128 * 64 * rec)
-    assert kda.workspace_size(1, 8192, 8, 1) == al((128 + 1) * 8 * rec) + al(8) + al(129 * 8) + al(8) + al(4)
+    assert kda.workspace_size(1, 8192, 64, 8) == (al((128 + 8) * 64 * rec) + al(8 * 8) + al((128 + 8) * 8)
+                                               + al(8 * 8) + al(8 * 4))
+    # varlen: one sequence of 8192 tokens on 8 heads (average 128 chunks): 8 segments
+    assert kda.workspace_size(1, 8192, 8, 1) == (al((128 + 1) * 8 * rec) + al(8) + al(129 * 8) + al(8) + al(4)
+                                              + al(nseg * 8 * m) + al(nseg * 8 * i))
+    # two sequences on 8 heads averaging 64 chunks: too short to gain 15%, no segments;
+    # averaging 256 chunks: 4 segments per sequence
+    assert kda.workspace_size(1, 8192, 8, 2) == (al((128 + 2) * 8 * rec) + al(16) + al(130 * 8) + al(16) + al(8))
+    assert kda.workspace_size(1, 32768, 8, 2) == (al((512 + 2) * 8 * rec) + al(16) + al(514 * 8) + al(16) + al(8)
+                                               + al(2 * 4 * 8 * m) + al(2 * 4 * 8 * i))

@@ -419,12 +419,15 @@ SEG_SHAPES = [
     (dict(B=2, T=4000, H=2, state='bf16', final='bf16', lower_bound=-0.05), 4),       # ragged last chunk
     (dict(B=1, T=4096, H=1, final=None, lower_bound=-0.3), 8),                        # stateless, no final state
     (dict(B=1, T=4096, H=2, state='fp32', lower_bound=-5.0), 8),                      # short memory
+    (dict(lengths=[4096], H=2, state='fp32', lower_bound=-0.01), 8),                  # varlen, one sequence
+    # varlen, uneven: 94, 40, 2 and 0 chunks in 4 segments each (empty segments included)
+    (dict(lengths=[6000, 2500, 70, 0], H=1, state='bf16', final='bf16', lower_bound=-0.05), 4),
 ]
 
 
 @pytest.mark.parametrize("shape,nseg", SEG_SHAPES,
                          ids=["T4096_H2_fp32_lb0.01", "B2_T4000_H2_bf16_lb0.05", "T4096_H1_nofinal_lb0.3",
-                              "T4096_H2_fp32_lb5"])
+                              "T4096_H2_fp32_lb5", "varlen_4096_H2", "varlen_uneven_H1_bf16"])
 def test_segmented_chain(shape, nseg, capfd, monkeypatch):
     w = kda_inputs.custom(**shape)
     say(f"segmented chain {shape}")
