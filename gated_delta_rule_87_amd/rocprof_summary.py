@@ -25,7 +25,7 @@ import os
 import statistics
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-KERNELS = ("kda_sched_kernel", "kda_intra_kernel", "kda_chain_kernel", "kda_recurrent_kernel")
+KERNELS = ("kda_sched_kernel", "kda_intra_kernel", "kda_chain_kernel", "kda_scan_kernel", "kda_recurrent_kernel")
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 GIB = 1 << 30
 
