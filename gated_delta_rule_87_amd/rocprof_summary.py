@@ -66,12 +66,19 @@ def counters(d):
 
 
 def kernel_stats(d):
+    """Per short kernel name; instantiations of one kernel (template arguments) are merged."""
     out = {}
     for r in csv.DictReader(open(one_file(d, "kernel_stats.csv"))):
         k = short_name(r["Name"])
-        if k is not None:
-            out[k] = {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
-                      "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3}
+        if k is None:
+            continue
+        e = out.setdefault(k, {"calls": 0, "total_ns": 0.0, "min_us": float("inf"), "max_us": 0.0})
+        e["calls"] += int(r["Calls"])
+        e["total_ns"] += float(r["TotalDurationNs"])
+        e["min_us"] = min(e["min_us"], float(r["MinNs"]) / 1e3)
+        e["max_us"] = max(e["max_us"], float(r["MaxNs"]) / 1e3)
+    for e in out.values():
+        e["avg_us"] = e["total_ns"] / e["calls"] / 1e3
     return out
 
 
