@@ -473,3 +473,16 @@ def test_segmented_chain_tp8_share_sampled():
     o, f = run(d, w)
     ro, rf = oracle_for(d, heads=heads)
     check(o, f, ro, rf, w.final, w.name, heads=heads)
+
+
+def test_segmented_chain_long_single_sequence(capfd, monkeypatch):
+    """131072 tokens on one head: 32 segments of 64 chunks and a 32-step scan, with a
+    long-memory gate so every segment's map carries the state."""
+    w = kda_inputs.custom(B=1, T=131072, H=1, state='fp32', lower_bound=-0.01)
+    say(f"long single sequence {w.T} tokens, segmented chain")
+    d = kda_inputs.make_inputs(w)
+    monkeypatch.setenv("KDA_LOG", "1")
+    o, f = run(d, w)
+    assert "segments=32" in capfd.readouterr().err
+    ro, rf = oracle_for(d)
+    check(o, f, ro, rf, 'fp32', "131072 tokens, 32 segments")
