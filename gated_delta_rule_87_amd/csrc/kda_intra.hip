@@ -41,20 +41,28 @@ namespace {
 
 constexpr int AROW = 68;   // floats per row of the padded 64x64 fp32 A matrix
 
+// 53,504 bytes, so that three workgroups share a compute unit's 160 KiB. The region
+// 'r' is reused three times: the gate constants and gram column fragments until the
+// off-diagonal grams are formed (phases A-D), then A until Tm is solved (phases D-E),
+// then V^T for phase F.
 struct IntraSmem {
-  float tot[4][KD];          // sub-chunk gate totals
-  float exref[4][KD];        // exp(reference point of sub-chunk w)          <= 1
-  float eend[4][KD];         // exp(total of sub-chunk w)                     <= 1
-  float c2[4][KD];           // exp(G_L - reference point of sub-chunk w+1)   <= 1
   float beta[CH];            // sigmoid(beta logits), 0 for padded tokens
   union {
-    u32x4 tk[4][4][64];      // off-diagonal gram column fragments [sub-chunk][k-step][lane]
-    float tm[CH * CH];       // then Tm, rows XOR-swizzled (see tmi)
-  } u;
+    struct {
+      float tot[4][KD];      // sub-chunk gate totals
+      float exref[4][KD];    // exp(reference point of sub-chunk w)          <= 1
+      float eend[4][KD];     // exp(total of sub-chunk w)                     <= 1
+      float c2[4][KD];       // exp(G_L - reference point of sub-chunk w+1)   <= 1
+      u32x4 tk[3][4][64];    // off-diagonal gram column fragments [sub-chunk][k-step][lane]
+                             // (sub-chunk 3 is never the column block of a later one)
+    } g;
+    float A[CH][AROW];       // beta * gram, strictly lower (blocks on and below the diagonal)
+    u32x4 vt[8][2][64];      // V^T bf16 fragments [value tile][token k-step][lane]
+  } r;
+  float tm[CH * CH];         // Tm, rows XOR-swizzled (see tmi)
   u32x4 kgt[8][2][64];       // (K^.Gamma)^T fp16 fragments [channel tile][token k-step][lane]
-  u32x4 vt[8][2][64];        // V^T bf16 fragments [value tile][token k-step][lane]
-  float A[CH][AROW];         // beta * gram, strictly lower (blocks on and below the diagonal)
 };
+static_assert(sizeof(IntraSmem) <= 163840 / 3, "three workgroups per compute unit");
 
 // swizzled index of Tm[r][c]: 16-byte column groups XORed with the row, so that
 // 16 lanes reading 16 consecutive rows at one column hit 16 different banks
@@ -118,24 +126,24 @@ template <int W>
 __device__ __forceinline__ void solve_column_block(IntraSmem& sm, int lt, int gq) {
   f32x4 Tc[4 - W];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) Tc[0][i] = sm.u.tm[tmi(16 * W + 4 * gq + i, 16 * W + lt)];
+  for (int i = 0; i < 4; ++i) Tc[0][i] = sm.tm[tmi(16 * W + 4 * gq + i, 16 * W + lt)];
 #pragma unroll
   for (int a = W + 1; a < 4; ++a) {
     f32x4 X = {0, 0, 0, 0};
 #pragma unroll
     for (int m = W; m < a; ++m) {
-      const f32x4 av = *reinterpret_cast<const f32x4*>(&sm.A[16 * a + lt][16 * m + 4 * gq]);
+      const f32x4 av = *reinterpret_cast<const f32x4*>(&sm.r.A[16 * a + lt][16 * m + 4 * gq]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) X = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], Tc[m - W][i], X, 0, 0, 0);
     }
-    const f32x4 tv = *reinterpret_cast<const f32x4*>(&sm.u.tm[tmi(16 * a + lt, 16 * a + 4 * gq)]);
+    const f32x4 tv = *reinterpret_cast<const f32x4*>(&sm.tm[tmi(16 * a + lt, 16 * a + 4 * gq)]);
     f32x4 Y = {0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < 4; ++i) Y = __builtin_amdgcn_mfma_f32_16x16x4f32(tv[i], X[i], Y, 0, 0, 0);
     Y = -Y;
     Tc[a - W] = Y;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sm.u.tm[tmi(16 * a + 4 * gq + j, 16 * W + lt)] = Y[j];
+    for (int j = 0; j < 4; ++j) sm.tm[tmi(16 * a + 4 * gq + j, 16 * W + lt)] = Y[j];
   }
 }
 
@@ -199,7 +207,7 @@ constexpr float DIAG_RANGE2 = 118.0f;
 //             DIAG_RANGE2 take the same MFMA path; the others form their diagonal block
 //             with pair_step (a wave-uniform choice, per sub-chunk).
 template <bool UB>
-__global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
+__global__ __launch_bounds__(256, UB ? 2 : 3) void kda_intra_kernel(FwdParams p) {
   __shared__ IntraSmem sm;
   const int H = p.H;
   const int slot = blockIdx.x;
@@ -228,7 +236,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
   const size_t rowoff = ((size_t)(t0 + (valid ? tok : 0)) * H + h) * KD;
 
   // ---------------- phase A: loads, gate, sub-chunk cumulative sums, norms ----
-  u32x4 qraw[4], kraw[4], vraw[4];
+  u32x4 qraw[4], kraw[4];
   float Gs[32];   // sub-chunk cumulative gates in log2 units (exp2(Gs) = exp of the natural sums)
   float rq, rk;
   bool slow = false;   // (UB only) this sub-chunk's diagonal block is formed entry by entry
@@ -251,7 +259,6 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
     for (int s = 0; s < 4; ++s) {
       qraw[s] = load_row8(p.q + rowoff, s, gq, true);
       kraw[s] = load_row8(p.k + rowoff, s, gq, true);
-      vraw[s] = load_row8(p.v + rowoff, s, gq, true);
       graw[s] = load_row8(p.g + rowoff, s, gq, true);
     }
     const float braw = bf16_to_f32(p.beta[(size_t)(t0 + (valid ? tok : 0)) * H + h]);
@@ -263,7 +270,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
     }
     if (L < CH && !valid) {   // partial chunk: rows past its end are zero
 #pragma unroll
-      for (int s = 0; s < 4; ++s) qraw[s] = kraw[s] = vraw[s] = graw[s] = u32x4{0u, 0u, 0u, 0u};
+      for (int s = 0; s < 4; ++s) qraw[s] = kraw[s] = graw[s] = u32x4{0u, 0u, 0u, 0u};
     }
     float ssq = 0.0f, ssk = 0.0f;
 #pragma unroll
@@ -299,8 +306,8 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
     if (lt == 15) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        *reinterpret_cast<f32x4*>(&sm.tot[w][32 * s + 4 * gq]) = f32x4{Gs[8 * s], Gs[8 * s + 1], Gs[8 * s + 2], Gs[8 * s + 3]};
-        *reinterpret_cast<f32x4*>(&sm.tot[w][32 * s + 16 + 4 * gq]) =
+        *reinterpret_cast<f32x4*>(&sm.r.g.tot[w][32 * s + 4 * gq]) = f32x4{Gs[8 * s], Gs[8 * s + 1], Gs[8 * s + 2], Gs[8 * s + 3]};
+        *reinterpret_cast<f32x4*>(&sm.r.g.tot[w][32 * s + 16 + 4 * gq]) =
             f32x4{Gs[8 * s + 4], Gs[8 * s + 5], Gs[8 * s + 6], Gs[8 * s + 7]};
       }
     }
@@ -345,23 +352,22 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
   {
     const int c = tid & (KD - 1);
     const int wa = tid >> 7;   // this thread fills sub-chunks wa and wa + 2
-    const float t0v = sm.tot[0][c], t1v = sm.tot[1][c], t2v = sm.tot[2][c], t3v = sm.tot[3][c];
+    const float t0v = sm.r.g.tot[0][c], t1v = sm.r.g.tot[1][c], t2v = sm.r.g.tot[2][c], t3v = sm.r.g.tot[3][c];
     const float GL = t0v + t1v + t2v + t3v;
     const float rA = wa ? t0v : 0.0f, rA1 = wa ? t0v + t1v : t0v;                  // ref_wa, ref_wa+1
     const float rB = wa ? t0v + t1v + t2v : t0v + t1v, rB1 = wa ? GL : t0v + t1v + t2v;   // ref_wa+2, ref_wa+3
-    sm.exref[wa][c] = fast_exp2(rA);   // the totals are in log2 units
-    sm.eend[wa][c] = fast_exp2(rA1 - rA);
-    sm.c2[wa][c] = fast_exp2(GL - rA1);
-    sm.exref[wa + 2][c] = fast_exp2(rB);
-    sm.eend[wa + 2][c] = fast_exp2(rB1 - rB);
-    sm.c2[wa + 2][c] = fast_exp2(GL - rB1);
+    sm.r.g.exref[wa][c] = fast_exp2(rA);   // the totals are in log2 units
+    sm.r.g.eend[wa][c] = fast_exp2(rA1 - rA);
+    sm.r.g.c2[wa][c] = fast_exp2(GL - rA1);
+    sm.r.g.exref[wa + 2][c] = fast_exp2(rB);
+    sm.r.g.eend[wa + 2][c] = fast_exp2(rB1 - rB);
+    sm.r.g.c2[wa + 2][c] = fast_exp2(GL - rB1);
     if (tid < KD) reinterpret_cast<float*>(rec + OFF_GAML)[c] = fast_exp2(GL);
   }
   lds_barrier();
 
   // ---------------- phase B: operands, diagonal grams, permuted copies -------
   const u32x4 idh0 = perm_operand(lt, gq, 0, 0x3C00u), idh1 = perm_operand(lt, gq, 1, 0x3C00u);
-  const u32x4 idb0 = perm_operand(lt, gq, 0, 0x3F80u), idb1 = perm_operand(lt, gq, 1, 0x3F80u);
   const int half = (w & 1) * 8;   // byte offset of this sub-chunk's tokens inside a 32-token fragment
   u32x4 Rkh[4], Rqh[4];            // off-diagonal gram rows (fp16), kept for phase D
 #pragma unroll
@@ -369,13 +375,13 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
     float qf[8], kf[8], exr[8], een[8], cc2[8];
     unpack8(qraw[s], qf);
     unpack8(kraw[s], kf);
-    ld8f(&sm.exref[w][32 * s + 4 * gq], exr);
-    ld8f(&sm.eend[w][32 * s + 4 * gq], een);
-    ld8f(&sm.c2[w][32 * s + 4 * gq], cc2);
+    ld8f(&sm.r.g.exref[w][32 * s + 4 * gq], exr);
+    ld8f(&sm.r.g.eend[w][32 * s + 4 * gq], een);
+    ld8f(&sm.r.g.c2[w][32 * s + 4 * gq], cc2);
     float rke[8], rqe[8], cki[8], tk[8], kp[8], kg[8], qg[8];
     if (UB && slow) {   // diagonal block done in phase A; no 2^-Gs factor here
       float tot[8], kn[8], qn[8];
-      ld8f(&sm.tot[w][32 * s + 4 * gq], tot);
+      ld8f(&sm.r.g.tot[w][32 * s + 4 * gq], tot);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         kn[e] = kf[e] * rk;
@@ -408,7 +414,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
     }
     Rkh[s] = pk_f16(rke);
     Rqh[s] = pk_f16(rqe);
-    sm.u.tk[w][s][l] = pk_f16(tk);
+    if (w < 3) sm.r.g.tk[w][s][l] = pk_f16(tk);
     *reinterpret_cast<u32x4*>(rec + OFF_QG + ((w * 4 + s) * 64 + l) * 16) = pk_f16(qg);
     const u32x4 kph = pk_f16(kp), kgh = pk_f16(kg);
 #pragma unroll
@@ -420,8 +426,6 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
       *reinterpret_cast<u32x2*>(rec + OFF_KP + ((ct * 2 + (w >> 1)) * 64 + l) * 16 + half) = pk4_f16(dk);
       const f32x4 dg = mfma_f16(kgh, par ? idh1 : idh0, z);
       *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(&sm.kgt[ct][w >> 1][l]) + half) = pk4_f16(dg);
-      const f32x4 dv = mfma_bf16(vraw[s], par ? idb1 : idb0, z);
-      *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(&sm.vt[ct][w >> 1][l]) + half) = pk4_bf16(dv);
     }
   }
   lds_barrier();
@@ -434,7 +438,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
     if (w >= 1) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const u32x4 tb = sm.u.tk[w - 1][s][l];
+        const u32x4 tb = sm.r.g.tk[w - 1][s][l];
         aO[0] = mfma_f16(Rkh[s], tb, aO[0]);
         qO[0] = mfma_f16(tb, Rqh[s], qO[0]);
       }
@@ -443,9 +447,9 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         float d2[8];
-        ld8f(&sm.eend[w - 1][32 * s + 4 * gq], d2);   // exp(ref_w - ref_{w-1})
+        ld8f(&sm.r.g.eend[w - 1][32 * s + 4 * gq], d2);   // exp(ref_w - ref_{w-1})
         const u32x4 dh = pk_f16(d2);
-        const u32x4 tb = sm.u.tk[w - 2][s][l];
+        const u32x4 tb = sm.r.g.tk[w - 2][s][l];
         aO[1] = mfma_f16(mul_f16x8(Rkh[s], dh), tb, aO[1]);
         qO[1] = mfma_f16(tb, mul_f16x8(Rqh[s], dh), qO[1]);
       }
@@ -454,27 +458,28 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         float d2[8], d1[8];
-        ld8f(&sm.eend[2][32 * s + 4 * gq], d2);
-        ld8f(&sm.eend[1][32 * s + 4 * gq], d1);
+        ld8f(&sm.r.g.eend[2][32 * s + 4 * gq], d2);
+        ld8f(&sm.r.g.eend[1][32 * s + 4 * gq], d1);
 #pragma unroll
         for (int e = 0; e < 8; ++e) d2[e] *= d1[e];     // exp(ref_3 - ref_1)
         const u32x4 dh = pk_f16(d2);
-        const u32x4 tb = sm.u.tk[0][s][l];
+        const u32x4 tb = sm.r.g.tk[0][s][l];
         aO[2] = mfma_f16(mul_f16x8(Rkh[s], dh), tb, aO[2]);
         qO[2] = mfma_f16(tb, mul_f16x8(Rqh[s], dh), qO[2]);
       }
     }
+    lds_barrier();   // every wave is past its reads of the gram fragments and constants: A may overwrite them
     // rows r = 16w + 4gq + j, columns i = 16b + lt
     const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.beta[16 * w + 4 * gq]);
     if (UB && slow) {   // aD[j] = gram[lt][4gq + j]
       const float b = sm.beta[16 * w + lt];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sm.A[16 * w + lt][16 * w + 4 * gq + j] = (lt > 4 * gq + j) ? b * aD[j] : 0.0f;
+      for (int j = 0; j < 4; ++j) sm.r.A[16 * w + lt][16 * w + 4 * gq + j] = (lt > 4 * gq + j) ? b * aD[j] : 0.0f;
     } else {            // aD[j] = gram[4gq + j][lt]
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * gq + j;
-        sm.A[16 * w + r][16 * w + lt] = (r > lt) ? br[j] * aD[j] : 0.0f;
+        sm.r.A[16 * w + r][16 * w + lt] = (r > lt) ? br[j] * aD[j] : 0.0f;
       }
     }
 #pragma unroll
@@ -482,7 +487,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
       if (w >= d + 1) {
         const int b = w - 1 - d;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sm.A[16 * w + 4 * gq + j][16 * b + lt] = br[j] * aO[d][j];
+        for (int j = 0; j < 4; ++j) sm.r.A[16 * w + 4 * gq + j][16 * b + lt] = br[j] * aO[d][j];
       }
     }
     // Aqk^T blocks: lane <-> query r = lt (tile w), registers <-> keys 16b + 4gq + j.
@@ -517,7 +522,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
       float acc = 0.0f;
 #pragma unroll
       for (int m4 = 0; m4 < i; m4 += 4) {
-        const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sm.A[16 * w + i][16 * w + m4]);
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sm.r.A[16 * w + i][16 * w + m4]);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
           if (m4 + u < i) acc += a4[u] * x[m4 + u];
@@ -526,13 +531,34 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
     }
     if (gq == 0) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sm.u.tm[tmi(16 * w + i, 16 * w + lt)] = x[i];
+      for (int i = 0; i < 16; ++i) sm.tm[tmi(16 * w + i, 16 * w + lt)] = x[i];
     }
   }
   lds_barrier();
   if (w == 0) solve_column_block<0>(sm, lt, gq);
   else if (w == 1) solve_column_block<1>(sm, lt, gq);
   else if (w == 2) solve_column_block<2>(sm, lt, gq);
+  lds_barrier();
+  {
+    // A is no longer needed: V^T takes its place. V is loaded only now, so it holds no
+    // registers through phases A-E.
+    const u32x4 idb0 = perm_operand(lt, gq, 0, 0x3F80u), idb1 = perm_operand(lt, gq, 1, 0x3F80u);
+    u32x4 vr[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) vr[s] = load_row8(p.v + rowoff, s, gq, true);
+    if (L < CH && !valid) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) vr[s] = u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        const f32x4 dv = mfma_bf16(vr[s], par ? idb1 : idb0, f32x4{0, 0, 0, 0});
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(&sm.r.vt[2 * s + par][w >> 1][l]) + half) = pk4_bf16(dv);
+      }
+    }
+  }
   lds_barrier();
 
   // ---------------- phase F: W = Tm diag(beta) K^.Gamma,  U~ = Tm diag(beta) V -
@@ -545,8 +571,8 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
     for (int s = 0; s <= smax; ++s) {
       // Tm diag(beta) row t at tokens m(e) = 32s + 4gq + e (e < 4), 32s + 16 + 4gq + e - 4 (e >= 4)
       const int m0 = 32 * s + 4 * gq, m1 = m0 + 16;
-      const f32x4 r0 = *reinterpret_cast<const f32x4*>(&sm.u.tm[tmi(t, m0)]);
-      const f32x4 r1 = *reinterpret_cast<const f32x4*>(&sm.u.tm[tmi(t, m1)]);
+      const f32x4 r0 = *reinterpret_cast<const f32x4*>(&sm.tm[tmi(t, m0)]);
+      const f32x4 r1 = *reinterpret_cast<const f32x4*>(&sm.tm[tmi(t, m1)]);
       const f32x4 b0 = *reinterpret_cast<const f32x4*>(&sm.beta[m0]);
       const f32x4 b1 = *reinterpret_cast<const f32x4*>(&sm.beta[m1]);
       float val[8], lo[8];
@@ -568,7 +594,7 @@ __global__ __launch_bounds__(256, 2) void kda_intra_kernel(FwdParams p) {
       for (int ct = 0; ct < 8; ++ct) accW[ct] = mfma_f16(sm.kgt[ct][s][l], tmh, accW[ct]);   // D[c][t]
 #pragma unroll
       for (int vt = 0; vt < 8; ++vt) {
-        const u32x4 vb = sm.vt[vt][s][l];
+        const u32x4 vb = sm.r.vt[vt][s][l];
         accU[vt] = mfma_bf16(hi, vb, accU[vt]);                                            // D[t][v]
         accU[vt] = mfma_bf16(lov, vb, accU[vt]);
       }
