@@ -32,11 +32,13 @@ fp32 final state). Prints ONE JSON line.
   cpu_baseline the fp64 CPU oracle timed on the host cores over the same
               workload (bounded: see "sample"), with a one-thread figure
 
-Timing: W warm-up steps, then K timed steps between HIP events on the launch
-stream; the steps alternate between two input sets (distinct tensors, the
-second drawn with the next seed) so that no step finds its inputs in the
-last-level cache from the step before. "path" also reports the median and the
-minimum per-call time.
+Timing: W warm-up steps (default 50: an idle GPU takes some milliseconds to
+raise its clocks, and the first tens of calls run up to 7% slower), then K timed
+steps between two HIP events on the launch stream, with nothing recorded between
+the calls except libkda's own per-kernel events (created without a system-scope
+fence, so they add little); the steps alternate between two input sets
+(distinct tensors, the second drawn with the next seed) so that no step finds
+its inputs in the last-level cache from the step before.
 """
 import argparse
 import json
@@ -123,7 +125,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=1, help="workload index (kda_inputs.workload)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--path", choices=["chunked", "recurrent"], default="chunked")
@@ -185,23 +187,22 @@ def main():
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     if args.path == "chunked":
         kda.profile_start(args.steps)
     t_wall = time.perf_counter()
+    start.record(stream)
     for i in range(args.steps):
-        starts[i].record(stream)
         step()
-        ends[i].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     per_kernel = kda.profile_stop() if args.path == "chunked" else {}
-    per_call_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    span_ms = starts[0].elapsed_time(ends[-1])
+    span_ms = start.elapsed_time(end)
     ms_per_step = span_ms / args.steps
-    call_ms = sum(per_call_ms) / len(per_call_ms)
+    call_ms = ms_per_step   # no events between the calls: they would add to the timed work
 
     state_in = state_out = 0
     if w.state is not None:
@@ -256,8 +257,7 @@ def main():
                            "traffic": recorded_traffic(w.name, dom) if safe else None,
                            "alg_bytes_per_launch": kd["alg_bytes"], "avg_launch_ms": kd["avg_ms"]}
     res["path"] = {"achieved_GBps": achieved, "frac_hbm": achieved / HBM_PEAK_GBS, "alg_bytes_per_call": alg_bytes,
-                   "call_ms": call_ms, "call_ms_median": sorted(per_call_ms)[len(per_call_ms) // 2],
-                   "call_ms_min": min(per_call_ms), "input_sets": 2, "mfma_tflops": flops / (call_ms * 1e-3) / 1e12,
+                   "call_ms": call_ms, "input_sets": 2, "mfma_tflops": flops / (call_ms * 1e-3) / 1e12,
                    "frac_mfma_bf16": flops / (call_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
     res["kernels"] = kernels
     res["wall_s_timed"] = t_wall

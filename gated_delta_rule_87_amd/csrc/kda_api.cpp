@@ -178,7 +178,8 @@ kda::FwdParams make_params(const void* q, const void* k, const void* v, const vo
 // ---- optional per-kernel timing of kda_fwd ---------------------------------
 // While enabled, each kda_fwd call takes the next slot of NK + 1 HIP events and
 // records one on the call's stream before its first kernel and one after each
-// kernel, so consecutive events bracket one kernel each.
+// kernel, so consecutive events bracket one kernel each (the event before the
+// scheduler only when the scheduler runs).
 constexpr int NK = 3;   // 0 varlen scheduler, 1 intra-chunk, 2 state chain + output
 const char* const kKernelNames[NK] = {"kda_sched_kernel", "kda_intra_kernel", "kda_chain_kernel"};
 
@@ -292,12 +293,14 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
                  (int)varlen, (long long)nseg);
 
   CallTimer tm(st);
-  hipError_t e = tm.mark(0);
-  if (e == hipSuccess && varlen && L.max_chunks > 0) {
-    e = kda::launch_sched(cu_seqlens, (int32_t)N, (int32_t)T, (int32_t)L.max_chunks,
-                          reinterpret_cast<int2*>(ws + L.seq_tab), reinterpret_cast<int2*>(ws + L.chunk_tab),
-                          reinterpret_cast<int2*>(ws + L.seq_span), reinterpret_cast<int32_t*>(ws + L.seq_order),
-                          st);
+  hipError_t e = hipSuccess;
+  if (varlen && L.max_chunks > 0) {   // (without the scheduler its interval is unused: no event)
+    e = tm.mark(0);
+    if (e == hipSuccess)
+      e = kda::launch_sched(cu_seqlens, (int32_t)N, (int32_t)T, (int32_t)L.max_chunks,
+                            reinterpret_cast<int2*>(ws + L.seq_tab), reinterpret_cast<int2*>(ws + L.chunk_tab),
+                            reinterpret_cast<int2*>(ws + L.seq_span), reinterpret_cast<int32_t*>(ws + L.seq_order),
+                            st);
     tm.launched(0);
   }
   if (e == hipSuccess) e = tm.mark(1);
@@ -377,7 +380,9 @@ int kda_profile_start(int max_calls) {
   P.ev.reserve((size_t)max_calls * (NK + 1));
   for (size_t i = 0; i < (size_t)max_calls * (NK + 1); ++i) {
     hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) {
+    // timing only: no system-scope fence (cache write-back) at each record, which would
+    // otherwise add several microseconds to every timed call
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
       profiler_release(P);
       return KDA_ERR_HIP;
     }

@@ -197,7 +197,10 @@ const char *kda_version(void);
  *
  * kda_profile_start(max_calls): from now on, each of the next max_calls
  *   kda_fwd calls records HIP events on its stream before its first kernel and
- *   after each kernel (the events are created here, not per call). Calls
+ *   after each kernel (the events are created here, not per call, with
+ *   hipEventDisableSystemFence: they only measure time and add no cache
+ *   write-back to the timed work, so they must not be used to order anything
+ *   with the host or other devices). Calls
  *   beyond max_calls are not timed. Starting again discards earlier recordings.
  *   Returns KDA_ERR_VALUE unless 1 <= max_calls <= 65536, KDA_ERR_HIP if an
  *   event cannot be created.
