@@ -82,6 +82,18 @@ def kernel_stats(d):
     return out
 
 
+def trace_durations(d):
+    """{kernel: [duration us of each launch, in dispatch order]} from the kernel trace."""
+    out = {}
+    rows = list(csv.DictReader(open(one_file(d, "kernel_trace.csv"))))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    for r in rows:
+        k = short_name(r["Kernel_Name"])
+        if k is not None:
+            out.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
@@ -92,6 +104,8 @@ def main():
     ap.add_argument("--copy-write", required=True)
     ap.add_argument("--sq", action="append", default=[])
     ap.add_argument("--bench-json", help="bench.py output line of the same workload (algorithmic bytes)")
+    ap.add_argument("--calls", type=int, default=0,
+                    help="kda_fwd calls in the traced run (warm-up + timed), to pick out the timed launches")
     ap.add_argument("--command-file", required=True, help="text file holding the exact commands that were run")
     ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
     a = ap.parse_args()
@@ -115,6 +129,7 @@ def main():
     for d in a.sq:
         sq.update(counters(d))
     stats = kernel_stats(a.trace)
+    durations = trace_durations(a.trace)
     alg = {}
     if a.bench_json:
         line = open(a.bench_json).read().strip().splitlines()[-1]
@@ -139,8 +154,19 @@ def main():
             fh.write("## rocprofv3 --kernel-trace --stats\n\n| calls | average us | min us | max us |\n|---|---|---|---|\n")
             fh.write(f"| {st['calls']} | {st['avg_us']:.1f} | {st['min_us']:.1f} | {st['max_us']:.1f} |\n\n")
             if k in alg:
+                # the timed calls are the last ones: average the trace over as many launches
+                # (a segmented chain launches the chain kernel twice per call)
+                per_call = max(1, round(st["calls"] / max(1, a.calls))) if a.calls else 1
+                tail = durations.get(k, [])[-alg[k]["launches"] * per_call:]
+                if tail and a.calls:
+                    fh.write(f"The same trace over the last {len(tail)} launches (the timed calls, after the "
+                             f"warm-up): {statistics.mean(tail):.1f} us average.\n\n")
                 fh.write(f"bench.py (HIP events on the launch stream, same command without the profiler): "
-                         f"{alg[k]['avg_ms'] * 1e3:.1f} us average over {alg[k]['launches']} launches.\n\n")
+                         f"{alg[k]['avg_ms'] * 1e3:.1f} us average over {alg[k]['launches']} calls")
+                if per_call > 1:
+                    fh.write(f", each interval the whole state-chain stage of a call ({per_call} launches of "
+                             f"this kernel and the scan kernel between them)")
+                fh.write(".\n\n")
             fh.write("## HBM traffic per launch (FETCH_SIZE, WRITE_SIZE; copy-calibrated)\n\n")
             fh.write("| counter | mean KiB per launch | scale | bytes |\n|---|---|---|---|\n")
             if fk:
