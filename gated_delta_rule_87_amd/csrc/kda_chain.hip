@@ -13,19 +13,23 @@
 // bf16 or fp32, dtypes equal when both are given) and out is written once in
 // place (2kiu.com guide, section 二).
 //
-// Wave roles (2 NW + 1 waves):
-//   state wave s < NW       keeps the fp32 state slice of value tile s in
-//                           registers; per chunk computes U and the new state;
-//                           publishes its fp16 operands (S0 and U, each row /
-//                           column scaled by a power of two) in LDS
-//   output wave NW + s      computes O^T of value tile s from those operands and
+// Wave roles (3 NW + 1 waves):
+//   state waves 2s, 2s + 1  keep the two channel halves of value tile s's fp32
+//                           state in registers; per chunk each forms half of U
+//                           (one token half, over all channels) and updates its
+//                           own channel half (from both token halves of U); each
+//                           publishes its fp16 operands (its half of S0 and of
+//                           U, scaled by powers of two) in LDS for the partner
+//                           and the output wave
+//   output wave 2 NW + s    computes O^T of value tile s from those operands and
 //                           the chunk's Q^.Gamma and Aqk, stores out
-//   DMA wave 2 NW           streams the records into LDS with buffer loads, 1.5
+//   DMA wave 3 NW           streams the records into LDS with buffer loads, 1.5
 //                           chunk steps ahead of their use
 // Two workgroup barriers per chunk: (A) the first part of chunk j's record and
 // S0's operands are in LDS; (B) the second part and U's operands are in LDS.
 // The state update runs while the output waves finish O, so neither the loads
-// nor the output sit on the state recurrence's critical path.
+// nor the output sit on the state recurrence's critical path; splitting each
+// tile's state over two waves halves the MFMA chain and the rescaling on it.
 //
 // Precision: MFMA operands are fp16. Each state row and each column of U is
 // scaled by its own power of two (max |x| * s in [1, 2)) before rounding, so
@@ -105,15 +109,15 @@ __device__ __forceinline__ constexpr int aqk_slot(int nt, int q) { return nt < 2
 constexpr int AQK_FRAG[6] = {0, 2, 4, 5, 6, 7};   // record fragment index (nt * 2 + q) of each slot
 
 template <int NW>
-struct ChainXchg {               // state wave -> output wave operands of one chunk
-  u32x4 sf[NW][4][64];           // S0 rows, fp16, scaled: MFMA A fragments per k-step
-  u32x4 uf[NW][2][64];           // U columns, fp16, scaled: MFMA A fragments per k-step
-  float iS[NW][16];              // 1 / row scale of S0
-  float iU[NW][16];              // 1 / column scale of U
+struct ChainXchg {               // operands of one chunk, shared by a tile's three waves
+  u32x4 sf[NW][4][64];           // S0 rows, fp16, scaled: MFMA fragments per k-step (channels 32q..)
+  u32x4 uf[NW][2][64];           // U columns, fp16, scaled: MFMA fragments per k-step (tokens 32q..)
+  float iS[NW][2][16];           // 1 / row scale of S0, per channel half
+  float iU[NW][2][16];           // 1 / column scale of U, per token half
 };
 
 template <int NW, int MODE>
-__global__ __launch_bounds__((2 * NW + 1) * 64) void kda_chain_kernel(FwdParams p, int nvg) {
+__global__ __launch_bounds__((3 * NW + 1) * 64) void kda_chain_kernel(FwdParams p, int nvg) {
   __shared__ ChainPart1<NW> r1[2];
   __shared__ ChainPart2<NW> r2[2];
   __shared__ ChainXchg<NW> xc;
@@ -171,7 +175,7 @@ __global__ __launch_bounds__((2 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
     len = p.map.T;
   }
 
-  if (w == 2 * NW) {
+  if (w == 3 * NW) {
     // ---------------- DMA wave ----------------
     // Straight into LDS with buffer loads: a scalar resource per record (which the
     // hardware range-checks), the lane offset in one VGPR, the in-record offset in an
@@ -242,56 +246,63 @@ __global__ __launch_bounds__((2 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
     return;
   }
 
-  const int s = w < NW ? w : w - NW;   // value tile of this wave within the group
-  const int vt = vg * NW + s;          // 16-wide value tile
+  // state waves 2s and 2s + 1 own the two channel halves of value tile s; output wave 2NW + s
+  const int s = w < 2 * NW ? (w >> 1) : w - 2 * NW;   // value tile of this wave within the group
+  const int vt = vg * NW + s;                         // 16-wide value tile
 
-  if (w < NW) {
+  if (w < 2 * NW) {
     // ---------------- state wave ----------------
-    // state slice, D layout of S^T: S[mt][j] = S[16 vt + lt][16 mt + 4 gq + j]
-    f32x4 S[8];
-    const size_t st_off = ((size_t)(n * H + h) * VD + 16 * vt + lt) * KD;
+    // Half hh of the tile's state: channels 64 hh .. 64 hh + 63, D layout of S^T:
+    // S[i][j] = S[16 vt + lt][16 (4 hh + i) + 4 gq + j]. Per chunk the wave forms U for
+    // token tiles 2hh, 2hh + 1 over all channels (its own half of S0 from registers, the
+    // partner's from LDS), then updates its own channel half from both token halves of U
+    // (its own from registers, the partner's from LDS). Every exchanged operand carries the
+    // power-of-two scale of its own half.
+    const int hh = w & 1;
+    f32x4 S[4];
+    const size_t st_off = ((size_t)(n * H + h) * VD + 16 * vt + lt) * KD + 64 * hh;
     // maps pass: tiles 0-7 are the value rows from a zero state (R), tiles 8-15 the rows
     // of the identity run without U~ (P); outputs pass: the scanned segment state
     const bool ptile = mode == CHAIN_MAPS && vt >= 8;
     if (mode == CHAIN_MAPS) {
       const int r = 16 * (vt - 8) + lt;   // identity row of a P tile
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) S[mt][jj] = (ptile && 16 * mt + 4 * gq + jj == r) ? 1.0f : 0.0f;
+        for (int jj = 0; jj < 4; ++jj) S[i][jj] = (ptile && 64 * hh + 16 * i + 4 * gq + jj == r) ? 1.0f : 0.0f;
     } else if (mode == CHAIN_OUTPUTS) {
       const float* src = p.seg.seg_init + st_off;
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) S[mt] = *reinterpret_cast<const f32x4*>(src + 16 * mt + 4 * gq);
+      for (int i = 0; i < 4; ++i) S[i] = *reinterpret_cast<const f32x4*>(src + 16 * i + 4 * gq);
     } else if (p.init_dtype == 2) {
       const float* src = static_cast<const float*>(p.init_state) + st_off;
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) S[mt] = *reinterpret_cast<const f32x4*>(src + 16 * mt + 4 * gq);
+      for (int i = 0; i < 4; ++i) S[i] = *reinterpret_cast<const f32x4*>(src + 16 * i + 4 * gq);
     } else if (p.init_dtype == 1) {
       const uint16_t* src = static_cast<const uint16_t*>(p.init_state) + st_off;
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const u32x2 r = *reinterpret_cast<const u32x2*>(src + 16 * mt + 4 * gq);
-        S[mt] = f32x4{bf16_lo(r.x), bf16_hi(r.x), bf16_lo(r.y), bf16_hi(r.y)};
+      for (int i = 0; i < 4; ++i) {
+        const u32x2 r = *reinterpret_cast<const u32x2*>(src + 16 * i + 4 * gq);
+        S[i] = f32x4{bf16_lo(r.x), bf16_hi(r.x), bf16_lo(r.y), bf16_hi(r.y)};
       }
     } else {
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0, 0, 0, 0};
+      for (int i = 0; i < 4; ++i) S[i] = f32x4{0, 0, 0, 0};
     }
 
-    // S0 -> fp16 operand fragments (k-step q: channel tiles 2q, 2q+1), each row v scaled
-    // by its own power of two; published for the output wave as well
+    // S0 half -> fp16 operand fragments (k-steps 2hh, 2hh + 1), each row v scaled by its own
+    // power of two; published for the partner and the output wave as well
     float iS;
-    u32x4 sf[4];
+    u32x4 sf[2];
     auto publish_state = [&]() {
       float sS;
-      pow2_scale(row_absmax(S, 8), sS, iS);
+      pow2_scale(row_absmax(S, 4), sS, iS);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < 2; ++q) {
         sf[q] = pack_pair_f16(S[2 * q], S[2 * q + 1], sS);
-        xc.sf[s][q][l] = sf[q];
+        xc.sf[s][2 * hh + q][l] = sf[q];
       }
-      if (gq == 0) xc.iS[s][lt] = iS;
+      if (gq == 0) xc.iS[s][hh][lt] = iS;
     };
     publish_state();
 
@@ -300,65 +311,69 @@ __global__ __launch_bounds__((2 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
       const ChainPart2<NW>& P2 = r2[j & 1];
       lds_barrier();   // (A)
 
-      // U = U~ + (-W) S0^T     D layout: lane <-> v, registers <-> tokens 16 mt + 4 gq + j
-      f32x4 U[4];
+      // U = U~ + (-W) S0^T for token tiles 2hh + i.  D layout: lane <-> v, registers <-> tokens
+      const u32x4 so0 = xc.sf[s][2 * (1 - hh)][l], so1 = xc.sf[s][2 * (1 - hh) + 1][l];
+      const float iSo = xc.iS[s][1 - hh][lt];
+      f32x4 U[2];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        f32x4 acc = {0, 0, 0, 0};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc = mfma_f16(P1.wneg[mt * 4 + q][l], sf[q], acc);
+      for (int i = 0; i < 2; ++i) {
+        const int mt = 2 * hh + i;
+        f32x4 am = {0, 0, 0, 0}, ao = {0, 0, 0, 0};
+        am = mfma_f16(P1.wneg[mt * 4 + 2 * hh][l], sf[0], am);
+        ao = mfma_f16(P1.wneg[mt * 4 + 2 * (1 - hh)][l], so0, ao);
+        am = mfma_f16(P1.wneg[mt * 4 + 2 * hh + 1][l], sf[1], am);
+        ao = mfma_f16(P1.wneg[mt * 4 + 2 * (1 - hh) + 1][l], so1, ao);
         const u32x2 uh = P1.ut[s][mt][l];
         const f32x2 u01 = unpack_f16x2(uh.x), u23 = unpack_f16x2(uh.y);
         const f32x4 ut = ptile ? f32x4{0, 0, 0, 0} : f32x4{u01.x, u01.y, u23.x, u23.y} * P1.usc[s * 64 + mt * 16 + lt];
-        U[mt] = ut + acc * iS;
+        U[i] = ut + am * iS + ao * iSo;
       }
       float sU, iU;
-      pow2_scale(row_absmax(U, 4), sU, iU);
-      u32x4 uf[2];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        uf[q] = pack_pair_f16(U[2 * q], U[2 * q + 1], sU);
-        xc.uf[s][q][l] = uf[q];
-      }
-      if (gq == 0) xc.iU[s][lt] = iU;
+      pow2_scale(row_absmax(U, 2), sU, iU);
+      const u32x4 uf = pack_pair_f16(U[0], U[1], sU);   // k-step hh of the state update
+      xc.uf[s][hh][l] = uf;
+      if (gq == 0) xc.iU[s][hh][lt] = iU;
       lds_barrier();   // (B)
 
-      // S1^T = Diag(Gamma_L) S0^T + K'^T U
+      // S1^T = Diag(Gamma_L) S0^T + K'^T U   (this wave's channel tiles 4hh + i)
+      const u32x4 ufo = xc.uf[s][1 - hh][l];
+      const float iUo = xc.iU[s][1 - hh][lt];
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
+      for (int i = 0; i < 4; ++i) {
+        const int mt = 4 * hh + i;
         const f32x4 g4 = *reinterpret_cast<const f32x4*>(&P2.gamw[128 + 16 * mt + 4 * gq]);
-        f32x4 acc = {0, 0, 0, 0};
-        acc = mfma_f16(P2.kp[mt * 2][l], uf[0], acc);
-        acc = mfma_f16(P2.kp[mt * 2 + 1][l], uf[1], acc);
-        S[mt] = S[mt] * g4 + acc * iU;
+        const f32x4 am = mfma_f16(P2.kp[mt * 2 + hh][l], uf, f32x4{0, 0, 0, 0});
+        const f32x4 ao = mfma_f16(P2.kp[mt * 2 + 1 - hh][l], ufo, f32x4{0, 0, 0, 0});
+        S[i] = S[i] * g4 + am * iU + ao * iUo;
       }
-      // the output wave has read S0's operands before (B); publish S1's for the next chunk
+      // the partner and the output wave have read S0's operands before (B); publish S1's
       publish_state();
     }
 
     if (mode == CHAIN_MAPS) {
-      float* dst = p.seg.maps + ((size_t)(n * H + h) * (2 * VD) + 16 * vt + lt) * KD;
+      float* dst = p.seg.maps + ((size_t)(n * H + h) * (2 * VD) + 16 * vt + lt) * KD + 64 * hh;
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(dst + 16 * mt + 4 * gq) = S[mt];
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4*>(dst + 16 * i + 4 * gq) = S[i];
     } else if (mode == CHAIN_OUTPUTS) {
       // the scan writes final_state
     } else if (p.final_dtype == 2) {
       float* dst = static_cast<float*>(p.final_state) + st_off;
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(dst + 16 * mt + 4 * gq) = S[mt];
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4*>(dst + 16 * i + 4 * gq) = S[i];
     } else if (p.final_dtype == 1) {
       uint16_t* dst = static_cast<uint16_t*>(p.final_state) + st_off;
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-        *reinterpret_cast<u32x2*>(dst + 16 * mt + 4 * gq) =
-            u32x2{pack_bf16x2(S[mt].x, S[mt].y), pack_bf16x2(S[mt].z, S[mt].w)};
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x2*>(dst + 16 * i + 4 * gq) =
+            u32x2{pack_bf16x2(S[i].x, S[i].y), pack_bf16x2(S[i].z, S[i].w)};
     }
     return;
   }
 
   // ---------------- output wave ----------------
   // O^T = scale (S0 Qg^T + U^T Aqk^T)   D layout: lane <-> token 16 nt + lt, registers <-> v.
-  // Register jj of lane group gq belongs to value row 4 gq + jj of the tile.
+  // Register jj of lane group gq belongs to value row 4 gq + jj of the tile. S0's channel
+  // halves and U's token halves each come with their own scales.
   const float scale = p.scale;
   if (mode == CHAIN_MAPS) {   // no outputs: keep the two barriers of every chunk step
     for (int j = 0; j < nc; ++j) {
@@ -374,27 +389,30 @@ __global__ __launch_bounds__((2 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
     u32x4 sf[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) sf[q] = xc.sf[s][q][l];
-    const f32x4 oS = *reinterpret_cast<const f32x4*>(&xc.iS[s][4 * gq]) * scale;
+    const f32x4 oS0 = *reinterpret_cast<const f32x4*>(&xc.iS[s][0][4 * gq]) * scale;
+    const f32x4 oS1 = *reinterpret_cast<const f32x4*>(&xc.iS[s][1][4 * gq]) * scale;
     f32x4 aq[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      aq[nt] = f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) aq[nt] = mfma_f16(sf[q], P1.qg[nt * 4 + q][l], aq[nt]);
-      aq[nt] *= oS;
+      f32x4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
+      a0 = mfma_f16(sf[0], P1.qg[nt * 4 + 0][l], a0);
+      a1 = mfma_f16(sf[2], P1.qg[nt * 4 + 2][l], a1);
+      a0 = mfma_f16(sf[1], P1.qg[nt * 4 + 1][l], a0);
+      a1 = mfma_f16(sf[3], P1.qg[nt * 4 + 3][l], a1);
+      aq[nt] = a0 * oS0 + a1 * oS1;
     }
     lds_barrier();   // (B)
     const u32x4 uf0 = xc.uf[s][0][l], uf1 = xc.uf[s][1][l];
-    const f32x4 oU = *reinterpret_cast<const f32x4*>(&xc.iU[s][4 * gq]) * scale;
+    const f32x4 oU0 = *reinterpret_cast<const f32x4*>(&xc.iU[s][0][4 * gq]) * scale;
+    const f32x4 oU1 = *reinterpret_cast<const f32x4*>(&xc.iU[s][1][4 * gq]) * scale;
     const int t0 = tok0 + j * CH;
     const int L = min(CH, len - j * CH);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      f32x4 aa = mfma_f16(uf0, P2.aqk[aqk_slot(nt, 0)][l], f32x4{0, 0, 0, 0});
-      if (nt >= 2) aa = mfma_f16(uf1, P2.aqk[aqk_slot(nt, 1)][l], aa);
+      f32x4 o = aq[nt] + mfma_f16(uf0, P2.aqk[aqk_slot(nt, 0)][l], f32x4{0, 0, 0, 0}) * oU0;
+      if (nt >= 2) o += mfma_f16(uf1, P2.aqk[aqk_slot(nt, 1)][l], f32x4{0, 0, 0, 0}) * oU1;
       const int tok = 16 * nt + lt;
       if (tok < L) {
-        const f32x4 o = aq[nt] + aa * oU;
         uint16_t* dst = p.out + ((size_t)(t0 + tok) * H + h) * VD + 16 * vt + 4 * gq;
         *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
       }
@@ -416,7 +434,7 @@ template <int NW>
 hipError_t launch_chain_nw(const FwdParams& p, int NH, int rows, hipStream_t stream) {
   const int nvg = rows / (16 * NW);
   const int64_t blocks = (int64_t)((NH + 7) / 8) * 8 * nvg;
-  const dim3 grid((unsigned)blocks), block((2 * NW + 1) * 64);
+  const dim3 grid((unsigned)blocks), block((3 * NW + 1) * 64);
   if (p.seg.mode == CHAIN_MAPS)
     hipLaunchKernelGGL((kda_chain_kernel<NW, CHAIN_MAPS>), grid, block, 0, stream, p, nvg);
   else if (p.seg.mode == CHAIN_OUTPUTS)
