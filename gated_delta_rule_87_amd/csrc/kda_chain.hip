@@ -405,17 +405,29 @@ __global__ __launch_bounds__((3 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
     const u32x4 uf0 = xc.uf[s][0][l], uf1 = xc.uf[s][1][l];
     const f32x4 oU0 = *reinterpret_cast<const f32x4*>(&xc.iU[s][0][4 * gq]) * scale;
     const f32x4 oU1 = *reinterpret_cast<const f32x4*>(&xc.iU[s][1][4 * gq]) * scale;
-    const int t0 = tok0 + j * CH;
     const int L = min(CH, len - j * CH);
+    // every product first, then the stores: a store under a per-lane condition would
+    // order each tile's LDS read, product and store one after another
+    u32x4 af[6];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) af[i] = P2.aqk[i][l];
+    u32x2 ob[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      f32x4 o = aq[nt] + mfma_f16(uf0, P2.aqk[aqk_slot(nt, 0)][l], f32x4{0, 0, 0, 0}) * oU0;
-      if (nt >= 2) o += mfma_f16(uf1, P2.aqk[aqk_slot(nt, 1)][l], f32x4{0, 0, 0, 0}) * oU1;
-      const int tok = 16 * nt + lt;
-      if (tok < L) {
-        uint16_t* dst = p.out + ((size_t)(t0 + tok) * H + h) * VD + 16 * vt + 4 * gq;
-        *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
-      }
+      f32x4 o = aq[nt] + mfma_f16(uf0, af[aqk_slot(nt, 0)], f32x4{0, 0, 0, 0}) * oU0;
+      if (nt >= 2) o += mfma_f16(uf1, af[aqk_slot(nt, 1)], f32x4{0, 0, 0, 0}) * oU1;
+      ob[nt] = u32x2{pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
+    }
+    // token 16 nt + lt of this chunk; consecutive tiles are 16 token rows apart
+    uint16_t* dst = p.out + ((size_t)(tok0 + j * CH + lt) * H + h) * VD + 16 * vt + 4 * gq;
+    const size_t tile_stride = (size_t)16 * H * VD;
+    if (L == CH) {   // full chunk (uniform): no per-lane condition
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) *reinterpret_cast<u32x2*>(dst + nt * tile_stride) = ob[nt];
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        if (16 * nt + lt < L) *reinterpret_cast<u32x2*>(dst + nt * tile_stride) = ob[nt];
     }
   }
 }
