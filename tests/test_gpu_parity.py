@@ -152,6 +152,30 @@ def test_beta_zero_zero_state_exact():
     assert np.all(o == 0) and np.all(f == 0)
 
 
+@pytest.mark.parametrize("path", ["chunked", "recurrent"])
+def test_edge_values(path):
+    """All-zero query and key rows (they normalise to zero, not NaN), beta logits of +inf
+    (beta = 1) and -inf (beta = 0), and rows scaled by 2^10 (the L2 norm removes the
+    scale), in and across chunks, against the oracle."""
+    w = kda_inputs.custom(B=1, T=200, H=2, state='fp32', lower_bound=-2.0, seed=3)
+    d = kda_inputs.make_inputs(w)
+    for t in (3, 64, 130):
+        d['q'][0, t] = 0
+    for t in (5, 65, 131, 199):
+        d['k'][0, t] = 0
+    for t in (7, 100):
+        d['beta'][0, t] = float('inf')
+    for t in (8, 101, 102):
+        d['beta'][0, t] = float('-inf')
+    for t in (20, 90):
+        d['q'][0, t] *= 1024
+        d['k'][0, t + 1] *= 1024
+    say(f"edge values (zero rows, beta logits +-inf, 2^10-scaled rows) path={path}")
+    ro, rf = oracle_for(d)
+    o, f = run(d, w, path)
+    check(o, f, ro, rf, 'fp32', f"edge values/{path}")
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads on sampled heads
 @pytest.mark.parametrize("idx,heads", [(1, [0, 21, 42, 63]), (2, [0, 33, 63]), (3, [0, 17, 62])])
