@@ -207,7 +207,7 @@ constexpr float DIAG_RANGE2 = 118.0f;
 //             DIAG_RANGE2 take the same MFMA path; the others form their diagonal block
 //             with pair_step (a wave-uniform choice, per sub-chunk).
 template <bool UB>
-__global__ __launch_bounds__(256, UB ? 2 : 3) void kda_intra_kernel(FwdParams p) {
+__global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
   __shared__ IntraSmem sm;
   const int H = p.H;
   const int slot = blockIdx.x;
@@ -372,42 +372,31 @@ __global__ __launch_bounds__(256, UB ? 2 : 3) void kda_intra_kernel(FwdParams p)
   u32x4 Rkh[4], Rqh[4];            // off-diagonal gram rows (fp16), kept for phase D
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    float qf[8], kf[8], exr[8], een[8], cc2[8];
+    float qf[8], kf[8], exr[8], cc2[8];
     unpack8(qraw[s], qf);
     unpack8(kraw[s], kf);
     ld8f(&sm.r.g.exref[w][32 * s + 4 * gq], exr);
-    ld8f(&sm.r.g.eend[w][32 * s + 4 * gq], een);
     ld8f(&sm.r.g.c2[w][32 * s + 4 * gq], cc2);
+    // exp(sub-chunk total) for the factorised path; (UB only) the total itself for a
+    // sub-chunk whose diagonal block was formed entry by entry in phase A, where exp(-G)
+    // may be out of fp32 range and exp(end_w - G) is taken directly
+    float en[8];
+    ld8f(UB && slow ? &sm.r.g.tot[w][32 * s + 4 * gq] : &sm.r.g.eend[w][32 * s + 4 * gq], en);
     float rke[8], rqe[8], cki[8], tk[8], kp[8], kg[8], qg[8];
-    if (UB && slow) {   // diagonal block done in phase A; no 2^-Gs factor here
-      float tot[8], kn[8], qn[8];
-      ld8f(&sm.r.g.tot[w][32 * s + 4 * gq], tot);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        kn[e] = kf[e] * rk;
-        qn[e] = qf[e] * rq;
-        const float ee = fast_exp2(Gs[8 * s + e]);   // <= 1 (may underflow to 0)
-        rke[e] = kn[e] * ee;
-        rqe[e] = qn[e] * ee;
-        tk[e] = kn[e] * fast_exp2(tot[e] - Gs[8 * s + e]);   // K^ exp(end_w - G) <= 1
-        kp[e] = tk[e] * cc2[e];
-        kg[e] = rke[e] * exr[e];
-        qg[e] = rqe[e] * exr[e];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float kn = kf[e] * rk, qn = qf[e] * rq;
-        const float ee = fast_exp2(Gs[8 * s + e]);  // <= 1
-        const float ie = fast_rcp(ee);              // <= e^80 (2^118 with an unbounded gate)
-        rke[e] = kn * ee;
-        rqe[e] = qn * ee;
-        cki[e] = kn * ie;
-        tk[e] = kn * (ie * een[e]);                 // K^ exp(end_w - G) <= 1
-        kp[e] = tk[e] * cc2[e];                     // K^ exp(G_L - G)   <= 1
-        kg[e] = rke[e] * exr[e];                    // K^ exp(G)         <= 1
-        qg[e] = rqe[e] * exr[e];                    // Q^ exp(G)         <= 1
-      }
+    for (int e = 0; e < 8; ++e) {
+      const float kn = kf[e] * rk, qn = qf[e] * rq;
+      const float ee = fast_exp2(Gs[8 * s + e]);  // <= 1 (may underflow to 0 on the entry-by-entry path)
+      const float ie = fast_rcp(ee);              // <= e^80 (2^118 with an unbounded gate)
+      rke[e] = kn * ee;
+      rqe[e] = qn * ee;
+      cki[e] = kn * ie;
+      tk[e] = kn * ((UB && slow) ? fast_exp2(en[e] - Gs[8 * s + e]) : ie * en[e]);   // K^ exp(end_w - G) <= 1
+      kp[e] = tk[e] * cc2[e];                     // K^ exp(G_L - G)   <= 1
+      kg[e] = rke[e] * exr[e];                    // K^ exp(G)         <= 1
+      qg[e] = rqe[e] * exr[e];                    // Q^ exp(G)         <= 1
+    }
+    if (!(UB && slow)) {   // diagonal gram blocks from the factorised operands
       const u32x4 rkd = pk_bf16(rke), ckd = pk_bf16(cki), rqd = pk_bf16(rqe);
       aD = mfma_bf16(rkd, ckd, aD);                 // D[r][i] = k^_r.k^_i exp(Gs_r - Gs_i)
       qD = mfma_bf16(ckd, rqd, qD);                 // D[i][r] = k^_i.q^_r exp(Gs_r - Gs_i)
