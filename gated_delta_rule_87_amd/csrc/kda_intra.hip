@@ -237,6 +237,10 @@ __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
 
   // ---------------- phase A: loads, gate, sub-chunk cumulative sums, norms ----
   u32x4 qraw[4], kraw[4];
+  // V rows: with the safe gate they are loaded with q, k and g (the kernel then needs 154
+  // VGPRs, still three workgroups per compute unit) and wait in registers until phase F;
+  // the unbounded-gate kernel has no registers to spare and loads them after the solve
+  u32x4 vr[4];
   float Gs[32];   // sub-chunk cumulative gates in log2 units (exp2(Gs) = exp of the natural sums)
   float rq, rk;
   bool slow = false;   // (UB only) this sub-chunk's diagonal block is formed entry by entry
@@ -261,6 +265,10 @@ __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
       kraw[s] = load_row8(p.k + rowoff, s, gq, true);
       graw[s] = load_row8(p.g + rowoff, s, gq, true);
     }
+    if constexpr (!UB) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) vr[s] = load_row8(p.v + rowoff, s, gq, true);
+    }
     const float braw = bf16_to_f32(p.beta[(size_t)(t0 + (valid ? tok : 0)) * H + h]);
     float dtf[32];
     if (fuse_gate) {
@@ -278,12 +286,13 @@ __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
       float gf[8];
       unpack8(graw[s], gf);
       if (fuse_gate) {
+        // rows past the chunk end take gate 0 through the outer factor (the inner terms are
+        // finite and >= 0 there), so no per-element select is needed
+        const float lb2v = valid ? lb2 : 0.0f, rate2v = valid ? rate2 : 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float gate2 = UB ? rate2 * softplus_log2((gf[e] + dtf[8 * s + e]) * LOG2E)
-                                 : lb2 * fast_rcp(1.0f + fast_exp2(rate2 * (gf[e] + dtf[8 * s + e])));
-          Gs[8 * s + e] = valid ? gate2 : 0.0f;
-        }
+        for (int e = 0; e < 8; ++e)
+          Gs[8 * s + e] = UB ? rate2v * softplus_log2((gf[e] + dtf[8 * s + e]) * LOG2E)
+                             : lb2v * fast_rcp(1.0f + fast_exp2(rate2 * (gf[e] + dtf[8 * s + e])));
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -529,12 +538,12 @@ __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
   else if (w == 2) solve_column_block<2>(sm, lt, gq);
   lds_barrier();
   {
-    // A is no longer needed: V^T takes its place. V is loaded only now, so it holds no
-    // registers through phases A-E.
+    // A is no longer needed: V^T takes its place.
     const u32x4 idb0 = perm_operand(lt, gq, 0, 0x3F80u), idb1 = perm_operand(lt, gq, 1, 0x3F80u);
-    u32x4 vr[4];
+    if constexpr (UB) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) vr[s] = load_row8(p.v + rowoff, s, gq, true);
+      for (int s = 0; s < 4; ++s) vr[s] = load_row8(p.v + rowoff, s, gq, true);
+    }
     if (L < CH && !valid) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) vr[s] = u32x4{0u, 0u, 0u, 0u};
