@@ -112,7 +112,9 @@ int check_common(const void* q, const void* k, const void* v, const void* g, con
                  uint32_t flags) {
   if (flags & ~(uint32_t)(KDA_FUSE_ALL | KDA_GATE_UNBOUNDED)) return KDA_ERR_VALUE;
   const bool gate_fused = (flags & KDA_FUSE_GATE) != 0;
-  if (!q || !k || !v || !g || !beta || !out) return KDA_ERR_NULL;
+  // with no tokens the token-indexed buffers hold no element (an empty tensor's data
+  // pointer may be NULL); no kernel reads or writes them then
+  if (T != 0 && (!q || !k || !v || !g || !beta || !out)) return KDA_ERR_NULL;
   if (gate_fused && (!A_log || !dt_bias)) return KDA_ERR_NULL;
   if (K != kda::KD || V != kda::VD) return KDA_ERR_SHAPE;
   if (B < 1 || T < 0 || H < 1 || H > (1 << 20)) return KDA_ERR_SHAPE;

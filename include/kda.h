@@ -138,7 +138,11 @@ size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N);
  *                                    Without it, each of the B rows is an
  *                                    independent sequence of length T.
  *   N            number of sequences (ignored without cu_seqlens)
- *   B, T, H, K, V                    sizes; K and V must be 128
+ *   B, T, H, K, V                    sizes; K and V must be 128. T may be 0:
+ *                                    then q, k, v, g, beta and out hold no
+ *                                    element and may be NULL, and the call
+ *                                    only writes final_state (the initial
+ *                                    state, or zeros, for every sequence)
  *   workspace, workspace_bytes       caller-owned device scratch of at least
  *                                    kda_fwd_workspace_size(B, T, H, N) bytes,
  *                                    256-byte aligned; its contents need no

@@ -95,6 +95,12 @@ def test_validation_errors(fn):
     # required pointers
     for name in ("q", "k", "v", "g", "beta", "out", "A_log", "dt_bias"):
         assert fn(**{name: None}) == ENULL, name
+    # T = 0: the token buffers hold no element and may be NULL (an empty tensor's data
+    # pointer); the checks after the pointer checks still apply (here: lower_bound)
+    empty = dict(q=None, k=None, v=None, g=None, beta=None, out=None)
+    assert fn(T=0, lb=-5.5, **empty) == EVALUE
+    assert fn(T=0, cu=FAKE, N=3, lb=-5.5, **empty) == EVALUE
+    assert fn(T=0, A_log=None, **empty) == ENULL                  # per-head parameters still required
     # state dtypes
     assert fn(init=FAKE, idt=7) == EDTYPE
     assert fn(init=FAKE, idt=1, fin=FAKE, fdt=2) == EDTYPE        # must match

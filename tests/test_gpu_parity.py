@@ -143,6 +143,28 @@ def test_out_fully_written_deterministic_and_aliasing():
     assert np.array_equal(out.float().double().cpu().numpy().reshape(-1, 2, 128), o1)
 
 
+@pytest.mark.parametrize("path", ["chunked", "recurrent"])
+@pytest.mark.parametrize("shape", [dict(B=2, T=0, H=3, state='fp32'),
+                                   dict(B=1, T=0, H=2, state='bf16', final='bf16'),
+                                   dict(B=2, T=0, H=2),
+                                   dict(lengths=[0, 0, 0], H=2, state='fp32')],
+                         ids=["fixed_fp32", "fixed_bf16", "fixed_stateless", "varlen_fp32"])
+def test_empty_input(shape, path):
+    """No tokens at all (T = 0: the token tensors are empty and their data pointers NULL):
+    final_state is written for every (sequence, head) and equals the initial state bit for
+    bit, or zeros without one; the oracle agrees."""
+    w = kda_inputs.custom(**shape)
+    say(f"empty input {shape} path={path}")
+    d = kda_inputs.make_inputs(w)
+    assert d['q'].numel() == 0
+    o, f = run(d, w, path)
+    ro, rf = oracle_for(d)
+    assert o.size == 0 and ro.size == 0
+    ref = d['initial_state'].double().numpy() if d['initial_state'] is not None else np.zeros_like(f)
+    assert np.array_equal(f, ref), "final_state differs from the initial state"
+    assert np.array_equal(rf, ref)
+
+
 def test_beta_zero_zero_state_exact():
     """beta logits -inf and no initial state: out and final_state are exactly 0."""
     w = kda_inputs.custom(T=150, H=2)
