@@ -200,11 +200,20 @@ __device__ __forceinline__ f32x4 reduce_scatter16(const float* P) {
 // step then sums at most 128 * 2^118 = 2^125 < FLT_MAX.
 constexpr float DIAG_RANGE2 = 118.0f;
 
+// Largest sub-chunk gate sum (log2 units) for the diagonal blocks factorised about each
+// channel's midpoint m = total / 2 instead of the sub-chunk start: the factors 2^(Gs - m)
+// and 2^(m - Gs) then stay within 2^(+-100), finite and (for key or query components
+// above 2^-26) clear of the subnormal range, and every kept entry, a product of the two
+// for i <= r, is at most 1. Entries above the diagonal may overflow; they are discarded
+// by the selects that mask the blocks.
+constexpr float DIAG_RANGE2_MID = 200.0f;
+
 // UB = false: the safe gate, g~ in [lower_bound, 0] with lower_bound >= -5, so a
 //             16-token sub-chunk spans at most 80 natural-log units and every diagonal
 //             block is formed from the factorised operands on MFMA.
 // UB = true : the gate without the safe bound. Sub-chunks whose gate sums stay within
-//             DIAG_RANGE2 take the same MFMA path; the others form their diagonal block
+//             DIAG_RANGE2 take the same MFMA path; those within DIAG_RANGE2_MID take it
+//             with the midpoint-referenced factors; the others form their diagonal block
 //             with pair_step (a wave-uniform choice, per sub-chunk).
 template <bool UB>
 __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
@@ -244,6 +253,7 @@ __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
   float Gs[32];   // sub-chunk cumulative gates in log2 units (exp2(Gs) = exp of the natural sums)
   float rq, rk;
   bool slow = false;   // (UB only) this sub-chunk's diagonal block is formed entry by entry
+  bool mid = false;    // (UB only) ... on MFMA, factorised about each channel's midpoint
   // diagonal gram block of this sub-chunk: D[r][i] = k^_r.k^_i exp(Gs_r - Gs_i) and
   // D[i][r] = k^_i.q^_r exp(Gs_r - Gs_i) in D layout (MFMA path, phase B); on the
   // entry-by-entry path (phase A) aD holds the first transposed, see phase D
@@ -310,7 +320,9 @@ __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
       float mn = Gs[0];
 #pragma unroll
       for (int i = 1; i < 32; ++i) mn = fminf(mn, Gs[i]);
-      slow = __builtin_amdgcn_readfirstlane(wave_min(mn) < -DIAG_RANGE2 ? 1 : 0) != 0;
+      const float wmn = wave_min(mn);
+      slow = __builtin_amdgcn_readfirstlane(wmn < -DIAG_RANGE2_MID ? 1 : 0) != 0;
+      mid = __builtin_amdgcn_readfirstlane(wmn < -DIAG_RANGE2 ? 1 : 0) != 0 && !slow;
     }
     if (lt == 15) {
 #pragma unroll
@@ -387,10 +399,11 @@ __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
     ld8f(&sm.r.g.exref[w][32 * s + 4 * gq], exr);
     ld8f(&sm.r.g.c2[w][32 * s + 4 * gq], cc2);
     // exp(sub-chunk total) for the factorised path; (UB only) the total itself for a
-    // sub-chunk whose diagonal block was formed entry by entry in phase A, where exp(-G)
-    // may be out of fp32 range and exp(end_w - G) is taken directly
+    // sub-chunk past DIAG_RANGE2 (diagonal block entry by entry in phase A, or about the
+    // midpoints), where exp(-G) may be out of fp32 range and exp(end_w - G) is taken directly
+    const bool direct = UB && (slow || mid);
     float en[8];
-    ld8f(UB && slow ? &sm.r.g.tot[w][32 * s + 4 * gq] : &sm.r.g.eend[w][32 * s + 4 * gq], en);
+    ld8f(direct ? &sm.r.g.tot[w][32 * s + 4 * gq] : &sm.r.g.eend[w][32 * s + 4 * gq], en);
     float rke[8], rqe[8], cki[8], tk[8], kp[8], kg[8], qg[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -400,12 +413,24 @@ __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
       rke[e] = kn * ee;
       rqe[e] = qn * ee;
       cki[e] = kn * ie;
-      tk[e] = kn * ((UB && slow) ? fast_exp2(en[e] - Gs[8 * s + e]) : ie * en[e]);   // K^ exp(end_w - G) <= 1
+      tk[e] = kn * (direct ? fast_exp2(en[e] - Gs[8 * s + e]) : ie * en[e]);   // K^ exp(end_w - G) <= 1
       kp[e] = tk[e] * cc2[e];                     // K^ exp(G_L - G)   <= 1
       kg[e] = rke[e] * exr[e];                    // K^ exp(G)         <= 1
       qg[e] = rqe[e] * exr[e];                    // Q^ exp(G)         <= 1
     }
-    if (!(UB && slow)) {   // diagonal gram blocks from the factorised operands
+    if (UB && mid) {       // the same products with the factors taken about m = total / 2
+      float mk[8], mq[8], mc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float hm = 0.5f * en[e], up = fast_exp2(Gs[8 * s + e] - hm);
+        mk[e] = kf[e] * rk * up;
+        mq[e] = qf[e] * rq * up;
+        mc[e] = kf[e] * rk * fast_exp2(hm - Gs[8 * s + e]);
+      }
+      const u32x4 rkd = pk_bf16(mk), ckd = pk_bf16(mc), rqd = pk_bf16(mq);
+      aD = mfma_bf16(rkd, ckd, aD);
+      qD = mfma_bf16(ckd, rqd, qD);
+    } else if (!(UB && slow)) {   // diagonal gram blocks from the factorised operands
       const u32x4 rkd = pk_bf16(rke), ckd = pk_bf16(cki), rqd = pk_bf16(rqe);
       aD = mfma_bf16(rkd, ckd, aD);                 // D[r][i] = k^_r.k^_i exp(Gs_r - Gs_i)
       qD = mfma_bf16(ckd, rqd, qD);                 // D[i][r] = k^_i.q^_r exp(Gs_r - Gs_i)
