@@ -97,3 +97,32 @@ def test_factorised_exponentials_stay_in_fp32_range():
     lb, SUB = -5.0, 16
     worst = -lb * SUB                               # |sum of 16 gates| < 80
     assert worst < math.log(np.finfo(np.float32).max)
+
+
+def test_midpoint_factorised_diagonal_block():
+    """Unbounded gate, sub-chunk gate sums in [-200, -118) (log2 units): the diagonal 16x16
+    blocks factorised about each channel's midpoint m = total / 2 keep both factors
+    2^(Gs - m) and 2^(m - Gs) within 2^(+-100), and in fp32 give every kept entry (key i <=
+    row r) finite and equal to the direct sum sum_c k_r k_i 2^(Gs_r - Gs_i); entries above
+    the diagonal may overflow, which is why the kernels mask them with selects."""
+    rng = np.random.default_rng(5)
+    SUB, K = 16, 128
+    for total in (-119.0, -150.0, -199.0):
+        # per-token log2 decays of one sub-chunk whose most negative channel sums to `total`
+        raw = rng.exponential(1.0, size=(SUB, K))
+        gates = -raw / raw.sum(0, keepdims=True).max() * (-total)
+        Gs = np.cumsum(gates, axis=0)                    # [token, channel], <= 0, decreasing
+        assert Gs.min() >= total - 1e-9 and Gs.min() < -118
+        m = 0.5 * Gs[-1]                                 # per-channel midpoint
+        up, dn = np.exp2(Gs - m), np.exp2(m - Gs)
+        assert np.log2(up).max() <= 100 and np.log2(dn).max() <= 100
+        k = rng.standard_normal((SUB, K))
+        k /= np.sqrt((k ** 2).sum(1, keepdims=True))
+        direct = np.einsum('rc,ic,ric->ri', k, k, np.exp2(Gs[:, None, :] - Gs[None, :, :]))
+        with np.errstate(over='ignore', invalid='ignore'):
+            f32 = (k * up).astype(np.float32) @ (k * dn).astype(np.float32).T
+        keep = np.tril(np.ones((SUB, SUB), bool))
+        assert np.isfinite(f32[keep]).all()
+        np.testing.assert_allclose(f32[keep], direct[keep], rtol=1e-4, atol=1e-6)
+        # the plain factorisation about the sub-chunk start would need 2^-Gs beyond 2^118
+        assert -Gs.min() > 118
