@@ -121,6 +121,7 @@ __global__ __launch_bounds__((3 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
   __shared__ ChainPart1<NW> r1[2];
   __shared__ ChainPart2<NW> r2[2];
   __shared__ ChainXchg<NW> xc;
+  __shared__ uint32_t touch_lds[64];   // landing window of the L2 touches (never read)
 
   const int H = p.H;
   constexpr int mode = MODE;   // ChainMode, fixed per instantiation
@@ -217,6 +218,22 @@ __global__ __launch_bounds__((3 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDSPTR(&d.gamw[0]), 16, lane16, GAM_WIN_OFF, 0, 0);
     };
     constexpr int N1 = 32 + 2 * NW + 1, N2 = 16 + 6 + 1;   // loads per part
+    // L2 touch of the record TD steps ahead (two value tiles per workgroup, plain chain):
+    // one dword of every 128-byte line, the nvg workgroups of a head taking every nvg-th
+    // line, so each line is requested once per head; lines past the record's end fall
+    // outside the resource's range and are dropped. The touches go to a scratch LDS
+    // window (no destination register), are issued after the wait that follows each
+    // first-part refill and count in the waits after it, which keeps every wait within
+    // the 63-load counter (N1 + N2 + TP = 63 for NW = 2).
+    constexpr int TP = (NW == 2 && MODE == CHAIN_FULL) ? 3 : 0, TD = 3;
+    static_assert(TP == 0 || N1 + N2 + TP <= 63, "touches must fit the load counter");
+    static_assert(TP == 0 || 64 * TP * (VD / 32) * 128 >= REC_BYTES, "touches cover the record");
+    auto touch = [&](int j) {
+      const __amdgpu_buffer_rsrc_t rs = rsrc(j);
+#pragma unroll
+      for (int i = 0; i < TP; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDSPTR(&touch_lds[0]), 4, (vg + nvg * (64 * i + l)) * 128, 0, 0, 0);
+    };
     if (nc > 0) {
       load_part1(0);
       load_part2(0);
@@ -229,16 +246,24 @@ __global__ __launch_bounds__((3 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
     }
     for (int j = 0; j < nc; ++j) {
       lds_barrier();                               // (A): P1(j) landed; P2 slot (j+1)&1 is free
+      const bool touched = TP > 0 && j >= 1 && j + TD - 1 < nc;   // T(j+TD-1) was issued in step j-1
       if (j + 1 < nc) {
         load_part2(j + 1);
-        wait_vmcnt<N1 + N2>();                     // P2(j) landed (P1(j+1), P2(j+1) may fly)
+        if (touched)                               // P2(j) landed (P1(j+1), T(j+TD-1), P2(j+1) may fly)
+          wait_vmcnt<N1 + TP + N2>();
+        else                                       // P2(j) landed (P1(j+1), P2(j+1) may fly)
+          wait_vmcnt<N1 + N2>();
       } else {
         wait_vmcnt<0>();
       }
       lds_barrier();                               // (B): P2(j) landed; P1 slot j&1 is free
       if (j + 2 < nc) {
         load_part1(j + 2);
-        wait_vmcnt<N2 + N1>();                     // P1(j+1) landed (P2(j+1), P1(j+2) may fly)
+        if (touched)                               // P1(j+1) landed (T(j+TD-1), P2(j+1), P1(j+2) may fly)
+          wait_vmcnt<TP + N2 + N1>();
+        else                                       // P1(j+1) landed (P2(j+1), P1(j+2) may fly)
+          wait_vmcnt<N2 + N1>();
+        if (TP > 0 && j + TD < nc) touch(j + TD);
       } else if (j + 1 < nc) {
         wait_vmcnt<N2>();
       }
