@@ -218,15 +218,16 @@ __global__ __launch_bounds__((3 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDSPTR(&d.gamw[0]), 16, lane16, GAM_WIN_OFF, 0, 0);
     };
     constexpr int N1 = 32 + 2 * NW + 1, N2 = 16 + 6 + 1;   // loads per part
-    // L2 touch of the record TD steps ahead (two value tiles per workgroup, plain chain):
+    // L2 touch of the record TD steps ahead (two value tiles per workgroup, every mode):
     // one dword of every 128-byte line, the nvg workgroups of a head taking every nvg-th
     // line, so each line is requested once per head; lines past the record's end fall
     // outside the resource's range and are dropped. The touches go to a scratch LDS
     // window (no destination register), are issued after the wait that follows each
     // first-part refill and count in the waits after it, which keeps every wait within
     // the 63-load counter (N1 + N2 + TP = 63 for NW = 2).
-    constexpr int TP = (NW == 2 && MODE == CHAIN_FULL) ? 3 : 0, TD = 3;
+    constexpr int TP = NW == 2 ? 3 : 0, TD = 3;
     static_assert(TP == 0 || N1 + N2 + TP <= 63, "touches must fit the load counter");
+    // nvg is VD / 32 (plain chain, outputs pass) or 2 VD / 32 (maps pass) with NW = 2
     static_assert(TP == 0 || 64 * TP * (VD / 32) * 128 >= REC_BYTES, "touches cover the record");
     auto touch = [&](int j) {
       const __amdgpu_buffer_rsrc_t rs = rsrc(j);
