@@ -313,12 +313,17 @@ def test_fusion_switches_off(shape, sw, path):
 # min(g, 0) unfused. The regimes steer the 16-token gate sums: "mild" keeps every
 # sub-chunk on the factorised MFMA path, "strong" and "unfused" push most sub-chunks
 # past it (entry-by-entry diagonal blocks), "mixed" puts huge and tiny per-channel
-# gates in the same sub-chunks and mixes both kinds of heads.
+# gates in the same sub-chunks and mixes both kinds of heads, "tiers" gives the heads
+# gate rates 3, 5.5 and 9 (the last H of them), whose 16-token sums put every sub-chunk
+# of a head on one diagonal-block form: factorised from the sub-chunk start, factorised
+# about the channel midpoints, entry by entry.
 def _unbounded_inputs(d, regime):
     d = dict(d)
     H, K = d['dt_bias'].shape
     if regime == "mild":
         d['A_log'] = torch.full((H,), -3.5)
+    elif regime == "tiers":
+        d['A_log'] = torch.log(torch.tensor([3.0, 5.5, 9.0][-H:]))
     elif regime == "mixed":
         al = torch.full((H,), math.log(16.0))
         al[0::2] = -3.0
@@ -334,7 +339,7 @@ def _unbounded_inputs(d, regime):
 
 
 @pytest.mark.parametrize("path", ["chunked", "recurrent"])
-@pytest.mark.parametrize("regime", ["mild", "strong", "mixed", "unfused"])
+@pytest.mark.parametrize("regime", ["mild", "strong", "mixed", "unfused", "tiers"])
 @pytest.mark.parametrize("shape", [dict(B=1, T=200, H=3, state='fp32', lower_bound=-3.0),
                                    dict(lengths=[70, 0, 130, 5, 64], H=2, state='bf16', final='bf16')],
                          ids=["fixed", "varlen"])
