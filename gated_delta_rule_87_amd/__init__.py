@@ -24,7 +24,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["fwd", "fwd_recurrent", "workspace_size", "lib", "KDAError", "status_string", "LIB_PATH",
+__all__ = ["fwd", "fwd_recurrent", "workspace_size", "record_bytes", "lib", "KDAError", "status_string", "LIB_PATH",
            "profile_start", "profile_stop"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -32,6 +32,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 STATE_NONE, STATE_BF16, STATE_FP32 = 0, 1, 2
 FUSE_GATE, FUSE_QK_L2NORM, FUSE_BETA_SIGMOID = 1, 2, 4
 GATE_UNBOUNDED = 8
+PATH_CHUNKED = 16
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE", 4: "KDA_ERR_VALUE",
            5: "KDA_ERR_ALIGN", 6: "KDA_ERR_WORKSPACE", 7: "KDA_ERR_HIP"}
 
@@ -95,6 +96,11 @@ def status_string(code: int) -> str:
 def workspace_size(B: int, T: int, H: int, N: int = 0) -> int:
     """Bytes of workspace kda_fwd needs (N = number of sequences with cu_seqlens, else 0)."""
     return int(lib().kda_fwd_workspace_size(int(B), int(T), int(H), int(N)))
+
+
+def record_bytes() -> int:
+    """Workspace bytes per 64-token chunk and head (the intra kernel's record)."""
+    return workspace_size(1, 64, 1, 0)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -173,8 +179,12 @@ def _stream_ptr(device) -> ctypes.c_void_p:
 def fwd(q, k, v, g, beta, scale: float, out, A_log, dt_bias, lower_bound: float,
         initial_state=None, final_state=None, cu_seqlens=None, workspace: Optional[torch.Tensor] = None,
         use_gate_in_kernel: bool = True, use_qk_l2norm_in_kernel: bool = True,
-        use_beta_sigmoid_in_kernel: bool = True, safe_gate: bool = True):
+        use_beta_sigmoid_in_kernel: bool = True, safe_gate: bool = True, force_chunked: bool = False):
     """Chunked KDA forward; writes ``out`` (and ``final_state``) in place, returns None.
+
+    Decode-sized calls (fixed length T <= 16, or varlen with at most two tokens per
+    sequence on average) run on the token-recurrent kernel instead, unless
+    ``force_chunked`` is set (KDA_PATH_CHUNKED of kda_fwd_ex).
 
     The three switches select the in-kernel input processing (default) or take
     that input as already processed: g as the log-decay (clamped into
@@ -184,6 +194,8 @@ def fwd(q, k, v, g, beta, scale: float, out, A_log, dt_bias, lower_bound: float,
     ignored (kda_fwd_ex in include/kda.h).
     """
     flags = _flags(use_gate_in_kernel, use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel, safe_gate)
+    if force_chunked:
+        flags |= PATH_CHUNKED
     B, T, H, K, V, N = _prepare(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens,
                                 gate_fused=use_gate_in_kernel)
     L = lib()

@@ -99,6 +99,17 @@ bool make_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool varlen, Layout
 
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Calls that kda_fwd / kda_fwd_ex hand to the token-recurrent kernel: fixed-length rows of
+// at most REC_MAX_T tokens, or varlen batches of at most REC_MAX_AVG tokens per sequence on
+// average (the lengths themselves stay on the device). The chunked path costs a full
+// 64-token chunk of intra-chunk work and one chain step per (sequence, head) whatever the
+// length, while the recurrent kernel's cost grows with each sequence's length; the
+// thresholds are where the two measured costs cross.
+constexpr int64_t REC_MAX_T = 16, REC_MAX_AVG = 2;
+inline bool short_call(int64_t T, int64_t N, bool varlen) {
+  return varlen ? T <= REC_MAX_AVG * N : T <= REC_MAX_T;
+}
+
 bool env_flag(const char* name) {
   const char* s = std::getenv(name);
   return s && s[0] == '1';
@@ -110,7 +121,7 @@ int check_common(const void* q, const void* k, const void* v, const void* g, con
                  const void* initial_state, int initial_dtype, const void* final_state, int final_dtype,
                  const int64_t* cu_seqlens, int64_t N, int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
                  uint32_t flags) {
-  if (flags & ~(uint32_t)(KDA_FUSE_ALL | KDA_GATE_UNBOUNDED)) return KDA_ERR_VALUE;
+  if (flags & ~(uint32_t)(KDA_FUSE_ALL | KDA_GATE_UNBOUNDED | KDA_PATH_CHUNKED)) return KDA_ERR_VALUE;
   const bool gate_fused = (flags & KDA_FUSE_GATE) != 0;
   // with no tokens the token-indexed buffers hold no element (an empty tensor's data
   // pointer may be NULL); no kernel reads or writes them then
@@ -263,9 +274,20 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
     rc = validate_cu_on_host(cu_seqlens, N, T, st);
     if (rc != KDA_OK) return rc;
   }
+  const bool force_chunked = (flags & KDA_PATH_CHUNKED) != 0;
+  flags &= ~(uint32_t)KDA_PATH_CHUNKED;
 
   kda::FwdParams p = make_params(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                                  initial_dtype, final_state, final_dtype, H, flags);
+  if (!force_chunked && short_call(T, N, varlen)) {   // decode-sized: token by token
+    p.map.T = (int32_t)T;
+    p.map.nseq = (int32_t)(varlen ? N : B);
+    if (env_flag("KDA_LOG"))
+      std::fprintf(stderr, "[kda] fwd B=%lld T=%lld H=%lld N=%lld path=recurrent\n", (long long)B, (long long)T,
+                   (long long)H, (long long)N);
+    const hipError_t e = kda::launch_recurrent(p, cu_seqlens, st);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  }
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   p.rec = ws + L.rec;
   p.map.T = (int32_t)T;
@@ -341,6 +363,7 @@ int kda_fwd_recurrent_ex(const void* q, const void* k, const void* v, const void
                          const void* initial_state, int initial_dtype, void* final_state, int final_dtype,
                          const int64_t* cu_seqlens, int64_t N, int64_t B, int64_t T, int64_t H, int64_t K,
                          int64_t V, uint32_t flags, void* stream) {
+  if (flags & KDA_PATH_CHUNKED) return KDA_ERR_VALUE;
   int rc = check_common(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state, initial_dtype,
                         final_state, final_dtype, cu_seqlens, N, B, T, H, K, V, flags);
   if (rc != KDA_OK) return rc;

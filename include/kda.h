@@ -91,7 +91,9 @@ enum kda_fuse_flags {
     KDA_FUSE_QK_L2NORM = 2,
     KDA_FUSE_BETA_SIGMOID = 4,
     KDA_FUSE_ALL = 7,
-    KDA_GATE_UNBOUNDED = 8
+    KDA_GATE_UNBOUNDED = 8,
+    KDA_PATH_CHUNKED = 16   /* kda_fwd_ex only: never hand a short call to the
+                               token-recurrent kernel (see kda_fwd)             */
 };
 
 /* State dtype codes for initial_state / final_state. */
@@ -149,6 +151,13 @@ size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N);
  *                                    initialisation and are clobbered
  *   stream       hipStream_t as void*
  * Returns a kda_status.
+ *
+ * Decode-sized calls run on the token-recurrent kernel of kda_fwd_recurrent,
+ * which computes the same operation without the chunked form's fixed cost of
+ * one 64-token chunk per (sequence, head): fixed-length calls with T <= 16, and
+ * varlen calls with T <= 2 N (at most two tokens per sequence on average; the
+ * lengths themselves stay on the device). The workspace rules are unchanged.
+ * kda_fwd_ex with KDA_PATH_CHUNKED keeps such calls on the chunked kernels.
  */
 int kda_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
             float scale, void *out, const float *A_log, const float *dt_bias, float lower_bound,
@@ -173,8 +182,8 @@ int kda_fwd_recurrent(const void *q, const void *k, const void *v, const void *g
 
 /*
  * kda_fwd_ex, kda_fwd_recurrent_ex -- kda_fwd / kda_fwd_recurrent with the
- * switches in `flags` (KDA_FUSE_* bits and KDA_GATE_UNBOUNDED; other bits:
- * KDA_ERR_VALUE). Every other argument and rule is that of the plain entry
+ * switches in `flags` (KDA_FUSE_* bits, KDA_GATE_UNBOUNDED and, for kda_fwd_ex,
+ * KDA_PATH_CHUNKED; other bits: KDA_ERR_VALUE). Every other argument and rule is that of the plain entry
  * point, except that A_log and dt_bias may be NULL when KDA_FUSE_GATE is
  * clear, and lower_bound is ignored when KDA_GATE_UNBOUNDED is set.
  */

@@ -180,8 +180,14 @@ def call_ex(flags, recurrent=False, **kw):
 def test_fusion_flag_validation(recurrent):
     """Unknown flag bits are rejected; A_log/dt_bias are required only with the fused gate
     (a later shape error shows the NULL pointers passed the pointer checks)."""
-    for bad in (0x10, 0x20, 0xffffffff):
+    for bad in (0x20, 0x40, 0xffffffff):
         assert call_ex(bad, recurrent) == EVALUE
+    # KDA_PATH_CHUNKED (0x10) is a kda_fwd_ex switch only; there it passes the flag check
+    # (the later shape error shows it)
+    if recurrent:
+        assert call_ex(0x10 | 7, recurrent) == EVALUE
+    else:
+        assert call_ex(0x10 | 7, recurrent, K=64) == ESHAPE
     assert call_ex(7, recurrent, A_log=None) == ENULL
     assert call_ex(7, recurrent, dt_bias=None) == ENULL
     assert call_ex(1, recurrent, dt_bias=None) == ENULL

@@ -57,7 +57,7 @@ def run_and_read(lengths, H=1):
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=device)
     out = torch.empty(1, T, H, 128, dtype=torch.bfloat16, device=device)
     kda.fwd(x['q'], x['k'], x['v'], x['g'], x['beta'], x['scale'], out, x['A_log'], x['dt_bias'],
-            x['lower_bound'], cu_seqlens=x['cu_seqlens'], workspace=ws)
+            x['lower_bound'], cu_seqlens=x['cu_seqlens'], workspace=ws, force_chunked=True)
     torch.cuda.synchronize()
     b = ws.cpu().numpy()
     max_chunks = T // 64 + N

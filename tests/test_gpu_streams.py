@@ -45,7 +45,7 @@ class Job:
         if self.path == "chunked":
             kda.fwd(x['q'], x['k'], x['v'], x['g'], x['beta'], x['scale'], self.out, x['A_log'], x['dt_bias'],
                     x['lower_bound'], initial_state=x['initial_state'], final_state=self.fin,
-                    cu_seqlens=x['cu_seqlens'], workspace=self.ws)
+                    cu_seqlens=x['cu_seqlens'], workspace=self.ws, force_chunked=True)
         else:
             kda.fwd_recurrent(x['q'], x['k'], x['v'], x['g'], x['beta'], x['scale'], self.out, x['A_log'],
                               x['dt_bias'], x['lower_bound'], initial_state=x['initial_state'],
