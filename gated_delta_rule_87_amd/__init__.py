@@ -182,7 +182,7 @@ def fwd(q, k, v, g, beta, scale: float, out, A_log, dt_bias, lower_bound: float,
         use_beta_sigmoid_in_kernel: bool = True, safe_gate: bool = True, force_chunked: bool = False):
     """Chunked KDA forward; writes ``out`` (and ``final_state``) in place, returns None.
 
-    Decode-sized calls (fixed length T <= 16, or varlen with at most two tokens per
+    Decode-sized calls (fixed length T <= 8, or varlen with at most two tokens per
     sequence on average) run on the token-recurrent kernel instead, unless
     ``force_chunked`` is set (KDA_PATH_CHUNKED of kda_fwd_ex).
 

@@ -154,7 +154,7 @@ size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N);
  *
  * Decode-sized calls run on the token-recurrent kernel of kda_fwd_recurrent,
  * which computes the same operation without the chunked form's fixed cost of
- * one 64-token chunk per (sequence, head): fixed-length calls with T <= 16, and
+ * one 64-token chunk per (sequence, head): fixed-length calls with T <= 8, and
  * varlen calls with T <= 2 N (at most two tokens per sequence on average; the
  * lengths themselves stay on the device). The workspace rules are unchanged.
  * kda_fwd_ex with KDA_PATH_CHUNKED keeps such calls on the chunked kernels.

@@ -227,3 +227,4 @@ def test_workspace_size_with_segmented_chain():
     assert kda.workspace_size(1, 8192, 8, 2) == (al((128 + 2) * 8 * rec) + al(16) + al(130 * 8) + al(16) + al(8))
     assert kda.workspace_size(1, 32768, 8, 2) == (al((512 + 2) * 8 * rec) + al(16) + al(514 * 8) + al(16) + al(8)
                                                + al(2 * 4 * 8 * m) + al(2 * 4 * 8 * i))
+

@@ -289,11 +289,11 @@ def test_edge_values(path):
 # ---------------------------------------------------------------------------
 # kda_fwd's own choice of path: decode-sized calls go to the token-recurrent kernel
 @pytest.mark.parametrize("shape,expect", [
-    (dict(B=2, T=16, H=3, state='fp32'), "recurrent"),
-    (dict(B=1, T=17, H=2, state='fp32', lower_bound=-1.0), "chunked"),
+    (dict(B=2, T=8, H=3, state='fp32'), "recurrent"),
+    (dict(B=1, T=9, H=2, state='fp32', lower_bound=-1.0), "chunked"),
     (dict(lengths=[1] * 20 + [3, 0], H=2, state='fp32'), "recurrent"),      # 23 tokens, 22 sequences
     (dict(lengths=[40, 1, 1, 2], H=2, state='bf16', final='bf16'), "chunked"),  # 44 tokens, 4 sequences
-], ids=["fixed_T16", "fixed_T17", "varlen_decode", "varlen_44_over_4"])
+], ids=["fixed_T8", "fixed_T9", "varlen_decode", "varlen_44_over_4"])
 def test_auto_path(shape, expect, capfd, monkeypatch):
     w = kda_inputs.custom(**shape)
     say(f"path chosen by kda_fwd for {shape}: expect {expect}")
