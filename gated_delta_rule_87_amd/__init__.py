@@ -34,7 +34,7 @@ FUSE_GATE, FUSE_QK_L2NORM, FUSE_BETA_SIGMOID = 1, 2, 4
 GATE_UNBOUNDED = 8
 PATH_CHUNKED = 16
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE", 4: "KDA_ERR_VALUE",
-           5: "KDA_ERR_ALIGN", 6: "KDA_ERR_WORKSPACE", 7: "KDA_ERR_HIP"}
+           5: "KDA_ERR_ALIGN", 6: "KDA_ERR_WORKSPACE", 7: "KDA_ERR_HIP", 8: "KDA_ERR_CAPACITY"}
 
 _lib = None
 
@@ -64,6 +64,11 @@ def _setup(L):
     L.kda_fwd_recurrent_ex.restype = I
     L.kda_fwd_recurrent_ex.argtypes = [P, P, P, P, P, F, P, P, P, F, P, I, P, I, P, I64, I64, I64, I64, I64,
                                        I64, U32, P]
+    L.kda_fwd_noalloc.restype = I
+    L.kda_fwd_noalloc.argtypes = [P, P, P, P, P, F, P, P, P, F, P, I, P, I, P, I64, I64, I64, I64, I64, I64, U32,
+                                  P]
+    L.kda_noalloc_capacity.restype = ctypes.c_size_t
+    L.kda_noalloc_capacity.argtypes = []
     L.kda_status_string.restype = ctypes.c_char_p
     L.kda_status_string.argtypes = [I]
     L.kda_version.restype = ctypes.c_char_p

@@ -15,7 +15,8 @@ LIB = os.path.join(HERE, "libkda.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 
-SOURCES = ["kda_api.cpp", "kda_sched.hip", "kda_intra.hip", "kda_chain.hip", "kda_scan.hip", "kda_recurrent.hip"]
+SOURCES = ["kda_api.cpp", "kda_sched.hip", "kda_intra.hip", "kda_chain.hip", "kda_scan.hip", "kda_recurrent.hip",
+           "kda_noalloc.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -400,6 +400,8 @@ const char* kda_status_string(int status) {
     case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: pointer not aligned (16 bytes; workspace 256 bytes)";
     case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or smaller than kda_fwd_workspace_size";
     case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP runtime or kernel launch error";
+    case KDA_ERR_CAPACITY:
+      return "KDA_ERR_CAPACITY: the call needs more workspace than kda_fwd_noalloc's fixed array (256 MiB) holds";
     default: return "KDA: unknown status";
   }
 }

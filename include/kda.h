@@ -61,7 +61,9 @@ enum kda_status {
                               contents (KDA_VALIDATE=1 only)                        */
     KDA_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                      */
     KDA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than kda_fwd_workspace_size */
-    KDA_ERR_HIP = 7        /* a HIP runtime call or kernel launch failed            */
+    KDA_ERR_HIP = 7,       /* a HIP runtime call or kernel launch failed            */
+    KDA_ERR_CAPACITY = 8   /* kda_fwd_noalloc: the call needs more workspace than
+                              its fixed device array holds (KDA_NOALLOC_CAPACITY)   */
 };
 
 /*
@@ -198,6 +200,36 @@ int kda_fwd_recurrent_ex(const void *q, const void *k, const void *v, const void
                          int initial_dtype, void *final_state, int final_dtype,
                          const int64_t *cu_seqlens, int64_t N, int64_t B, int64_t T, int64_t H,
                          int64_t K, int64_t V, uint32_t flags, void *stream);
+
+/*
+ * kda_fwd_noalloc -- kda_fwd_ex for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). The same operation, arguments, switches, rules and errors as
+ * kda_fwd_ex, without the workspace arguments: the workspace is a fixed array
+ * of KDA_NOALLOC_CAPACITY bytes in device memory that the library holds on
+ * every GPU it runs on, from its first use there until the process ends. The
+ * call itself allocates nothing and issues no memset or copy.
+ *   - Calls whose kda_fwd_workspace_size(B, T, H, N) exceeds the capacity are
+ *     rejected on the host with KDA_ERR_CAPACITY, before anything is launched
+ *     (256 MiB hold 3,500 chunk-heads at 74.5 KiB each, e.g. T = 4096 at
+ *     H = 54 or T = 2048 at H = 109; decode-sized calls need none at all).
+ *   - The array of the CURRENT device is used: `stream` must belong to it.
+ *     The array's device address is looked up once per device, on the first
+ *     call there (KDA_ERR_HIP if that fails).
+ *   - Every call on one GPU shares that GPU's array and leaves its contents
+ *     behind; nothing in it needs clearing (each call writes every word it
+ *     reads). Calls that overlap on one device (several streams or host
+ *     threads) RACE on the array: the caller must serialise them.
+ * kda_noalloc_capacity() returns KDA_NOALLOC_CAPACITY.
+ */
+#define KDA_NOALLOC_CAPACITY ((size_t)256 << 20)
+int kda_fwd_noalloc(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                    float scale, void *out, const float *A_log, const float *dt_bias,
+                    float lower_bound, const void *initial_state, int initial_dtype,
+                    void *final_state, int final_dtype, const int64_t *cu_seqlens, int64_t N,
+                    int64_t B, int64_t T, int64_t H, int64_t K, int64_t V, uint32_t flags,
+                    void *stream);
+size_t kda_noalloc_capacity(void);
 
 /* kda_status_string -- static description of a status code (never NULL). */
 const char *kda_status_string(int status);

@@ -17,7 +17,7 @@ import gated_delta_rule_87_amd as kda
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
 
-OK, ENULL, ESHAPE, EDTYPE, EVALUE, EALIGN, EWS, EHIP = range(8)
+OK, ENULL, ESHAPE, EDTYPE, EVALUE, EALIGN, EWS, EHIP, ECAP = range(9)
 FAKE = 0x10000000          # 256-byte aligned fake device address (never dereferenced)
 
 
@@ -31,7 +31,8 @@ def test_header_symbols_exported():
     names = declared_functions()
     assert {"kda_fwd", "kda_fwd_recurrent", "kda_fwd_workspace_size", "kda_status_string",
             "kda_version", "kda_profile_start", "kda_profile_stop", "kda_profile_kernel_count",
-            "kda_profile_kernel_name", "kda_fwd_ex", "kda_fwd_recurrent_ex"} <= set(names)
+            "kda_profile_kernel_name", "kda_fwd_ex", "kda_fwd_recurrent_ex", "kda_fwd_noalloc",
+            "kda_noalloc_capacity"} <= set(names)
     L = ctypes.CDLL(kda.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"libkda.so does not export {n}"
@@ -40,7 +41,7 @@ def test_header_symbols_exported():
 def test_version_and_status_strings():
     L = kda.lib()
     assert b"gfx950" in L.kda_version()
-    for code in range(8):
+    for code in range(9):
         s = kda.status_string(code)
         assert s.startswith("KDA_"), s
     assert "unknown" in kda.status_string(99)
@@ -228,3 +229,15 @@ def test_workspace_size_with_segmented_chain():
     assert kda.workspace_size(1, 32768, 8, 2) == (al((512 + 2) * 8 * rec) + al(16) + al(514 * 8) + al(16) + al(8)
                                                + al(2 * 4 * 8 * m) + al(2 * 4 * 8 * i))
 
+
+def test_noalloc_capacity_check_on_host():
+    """kda_fwd_noalloc rejects a call whose workspace exceeds its fixed array before any
+    HIP call (KDA_ERR_CAPACITY); the capacity is the header's 256 MiB."""
+    L = kda.lib()
+    cap = L.kda_noalloc_capacity()
+    assert cap == 256 << 20
+    assert kda.workspace_size(1, 8192, 64) > cap >= kda.workspace_size(1, 4096, 54)
+    P = ctypes.c_void_p
+    args = [P(FAKE)] * 5 + [0.088, P(FAKE), P(FAKE), P(FAKE), -5.0, None, 0, None, 0, None, 0]
+    assert L.kda_fwd_noalloc(*args, 1, 8192, 64, 128, 128, 7, None) == ECAP
+    assert L.kda_fwd_noalloc(*args, 2, 32768, 8, 128, 128, 7, None) == ECAP

@@ -1,0 +1,112 @@
+"""kda_fwd_noalloc (workspace in the library's fixed device array) against kda_fwd_ex
+with a caller workspace, through the C ABI: bit-identical results on consecutive calls,
+the later ones smaller than the first (the array keeps the earlier call's contents,
+which must not matter), and the host-side rejection of calls beyond the capacity."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs
+import gated_delta_rule_87_amd as kda
+from oracle import kda_oracle
+
+pytestmark = pytest.mark.gpu
+
+CAPACITY = 256 << 20
+KDA_ERR_CAPACITY = 8
+
+
+def say(*a):
+    print("[gpu-test]", *a, flush=True)
+
+
+def _call(entry, w, x, out, fin, ws=None, flags=7):
+    L = kda.lib()
+    B, T, H = x['q'].shape[:3]
+    N = w.n_seqs if x['cu_seqlens'] is not None else 0
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    code = lambda t: kda.STATE_NONE if t is None else (kda.STATE_FP32 if t.dtype == torch.float32 else kda.STATE_BF16)
+    st = x['initial_state']
+    stream = ctypes.c_void_p(torch.cuda.current_stream(x['q'].device).cuda_stream)
+    head = (P(x['q']), P(x['k']), P(x['v']), P(x['g']), P(x['beta']), x['scale'], P(out), P(x['A_log']),
+            P(x['dt_bias']), x['lower_bound'], P(st), code(st), P(fin), code(fin), P(x['cu_seqlens']), N, B, T, H,
+            128, 128, flags)
+    if entry == "noalloc":
+        return L.kda_fwd_noalloc(*head, stream)
+    return L.kda_fwd_ex(*head, P(ws), 0 if ws is None else ws.numel(), stream)
+
+
+def _run(entry, w, x):
+    device = x['q'].device
+    B, T, H = x['q'].shape[:3]
+    out = torch.full((B, T, H, 128), float('nan'), dtype=torch.bfloat16, device=device)
+    sdt = torch.float32 if w.final == 'fp32' else torch.bfloat16
+    fin = torch.full((w.n_seqs, H, 128, 128), float('nan'), dtype=sdt, device=device)
+    ws = None
+    if entry == "ex":
+        N = w.n_seqs if x['cu_seqlens'] is not None else 0
+        ws = torch.empty(max(1, kda.workspace_size(B, T, H, N)), dtype=torch.uint8, device=device)
+    rc = _call(entry, w, x, out, fin, ws)
+    assert rc == 0, kda.status_string(rc)
+    torch.cuda.synchronize()
+    return out, fin
+
+
+CASES = [
+    dict(lengths=[700, 3, 0, 1500, 64], H=4, state='fp32'),          # varlen: scheduler tables + records
+    dict(B=1, T=300, H=2, state='bf16', final='bf16', lower_bound=-2.0),   # smaller, fixed length
+    dict(B=1, T=4096, H=2, state='fp32', lower_bound=-0.05),         # segmented chain (maps and states)
+    dict(lengths=[1] * 30 + [2], H=3, state='fp32'),                  # decode-sized: the recurrent kernel
+    dict(B=2, T=130, H=1, state='fp32', lower_bound=-1.0),           # smaller again
+]
+
+
+def test_capacity_exported():
+    assert kda.lib().kda_noalloc_capacity() == CAPACITY
+
+
+@pytest.mark.parametrize("order", ["as_listed", "reversed"])
+def test_noalloc_matches_workspace_entry(order):
+    device = torch.device("cuda:0")
+    cases = CASES if order == "as_listed" else CASES[::-1]
+    for i, c in enumerate(cases):
+        w = kda_inputs.custom(**c)
+        N = w.n_seqs if w.lengths is not None else 0
+        assert kda.workspace_size(w.B, w.T, w.H, N) <= CAPACITY
+        say(f"no-alloc call {i}: {c}")
+        d = kda_inputs.make_inputs(w)
+        x = {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+        o1, f1 = _run("noalloc", w, x)
+        o2, f2 = _run("ex", w, x)
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), f"call {i}: out differs"
+        assert torch.equal(f1.view(torch.int16) if f1.dtype == torch.bfloat16 else f1,
+                           f2.view(torch.int16) if f2.dtype == torch.bfloat16 else f2), f"call {i}: final differs"
+        if i < 2:   # and against the oracle
+            ro, rf = kda_oracle(d['q'], d['k'], d['v'], d['g'], d['beta'], d['scale'], d['A_log'], d['dt_bias'],
+                                d['lower_bound'], initial_state=d['initial_state'], cu_seqlens=d['cu_seqlens'])
+            o = o1.float().double().cpu().numpy().reshape(ro.shape)
+            f = f1.float().double().cpu().numpy()
+            rel = np.linalg.norm(o - ro) / np.linalg.norm(ro)
+            frel = np.linalg.norm(f - rf) / np.linalg.norm(rf)
+            say(f"  oracle: out max-abs {np.abs(o - ro).max():.3e} rel-L2 {rel:.3e} final rel-L2 {frel:.3e}")
+            assert np.abs(o - ro).max() <= 2e-2 and rel <= 5e-3
+            assert frel <= (2e-3 if w.final == 'fp32' else 5e-3)
+
+
+def test_noalloc_rejects_beyond_capacity():
+    """T = 8192, H = 64 needs 625 MB of workspace: rejected on the host, nothing written."""
+    device = torch.device("cuda:0")
+    w = kda_inputs.custom(B=1, T=8192, H=64)
+    assert kda.workspace_size(1, 8192, 64, 0) > CAPACITY
+    z = torch.zeros(1, 8192, 64, 128, dtype=torch.bfloat16, device=device)
+    x = dict(q=z, k=z, v=z, g=z, beta=torch.zeros(1, 8192, 64, dtype=torch.bfloat16, device=device),
+             A_log=torch.zeros(64, device=device), dt_bias=torch.zeros(64, 128, device=device), scale=0.1,
+             lower_bound=-5.0, initial_state=None, cu_seqlens=None)
+    out = torch.full_like(z, float('nan'))
+    fin = torch.full((1, 64, 128, 128), float('nan'), device=device)
+    rc = _call("noalloc", w, x, out, fin)
+    assert rc == KDA_ERR_CAPACITY, kda.status_string(rc)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(out).all()) and bool(torch.isnan(fin).all()), "a rejected call wrote something"
