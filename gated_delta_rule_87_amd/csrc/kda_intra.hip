@@ -41,7 +41,7 @@ namespace {
 
 constexpr int AROW = 68;   // floats per row of the padded 64x64 fp32 A matrix
 
-// 53,504 bytes, so that three workgroups share a compute unit's 160 KiB. The region
+// 52,480 bytes, so that three workgroups share a compute unit's 160 KiB. The region
 // 'r' is reused three times: the gate constants and gram column fragments until the
 // off-diagonal grams are formed (phases A-D), then A until Tm is solved (phases D-E),
 // then V^T for phase F.
@@ -50,9 +50,10 @@ struct IntraSmem {
   union {
     struct {
       float tot[4][KD];      // sub-chunk gate totals
-      float exref[4][KD];    // exp(reference point of sub-chunk w)          <= 1
       float eend[4][KD];     // exp(total of sub-chunk w)                     <= 1
-      float c2[4][KD];       // exp(G_L - reference point of sub-chunk w+1)   <= 1
+      _Float16 exref_h[4][KD];   // exp(reference point of sub-chunk w)      <= 1, fp16
+      _Float16 eend_h[4][KD];    // eend in fp16
+      _Float16 c2_h[4][KD];      // exp(G_L - reference point of sub-chunk w+1) <= 1, fp16
       u32x4 tk[3][4][64];    // off-diagonal gram column fragments [sub-chunk][k-step][lane]
                              // (sub-chunk 3 is never the column block of a later one)
     } g;
@@ -96,6 +97,12 @@ __device__ __forceinline__ u32x4 load_row8(const uint16_t* row, int s, int gq, b
   const auto a = __builtin_amdgcn_permlane16_swap(x.x, x.z, false, false);
   const auto b = __builtin_amdgcn_permlane16_swap(x.y, x.w, false, false);
   return u32x4{a[0], b[0], a[1], b[1]};
+}
+// p -> fp16 channels +0..3 and +16..19, packed in the order pk_f16 gives
+__device__ __forceinline__ u32x4 ld8h(const _Float16* p) {
+  const u32x2 a = *reinterpret_cast<const u32x2*>(p);
+  const u32x2 b = *reinterpret_cast<const u32x2*>(p + 16);
+  return u32x4{a.x, a.y, b.x, b.y};
 }
 __device__ __forceinline__ void ld8f(const float* p, float* f) {   // p -> channels +0..3 and +16..19
   const f32x4 a = *reinterpret_cast<const f32x4*>(p);
@@ -195,26 +202,91 @@ __device__ __forceinline__ f32x4 reduce_scatter16(const float* P) {
   return r;
 }
 
+// Diagonal 16x16 gram blocks of one sub-chunk in the split form, for gate sums too large
+// for one reference point per channel (unbounded gate):
+//   - entries within one 8-token half: factors 2^(Gs - m) (rows) and 2^(m - Gs) (columns)
+//     about that half's per-channel midpoint m (g7 / 2 for the first half, (g7 + g15) / 2
+//     for the second, with g7, g15 the channel's sums at tokens 7 and 15), each within
+//     2^(+-span / 2) for a half whose gate sum spans at most span;
+//   - entries of a second-half row against a first-half column: factors 2^(Gs - g7)
+//     (rows) and 2^(g7 - Gs) (columns), both <= 1.
+// One product holds every within-half entry (each lane's token takes its own half's
+// midpoint), another the cross entries (rows of the first half and columns of the second
+// half are zero there); the entries are merged by half here, and the caller masks those
+// above the diagonal. Lane (gq, lt) holds token lt and the 32 channels of kraw / qraw /
+// Gs (log2 units).
+__device__ __forceinline__ void split_diag(const u32x4* qraw, const u32x4* kraw, const float* Gs, float rq, float rk,
+                                           int lt, int gq, f32x4& aD, f32x4& qD) {
+  const bool hi = lt >= 8;
+  f32x4 aX = {0, 0, 0, 0}, qX = {0, 0, 0, 0};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    float qf[8], kf[8];
+    unpack8(qraw[s], qf);
+    unpack8(kraw[s], kf);
+    uint32_t a1[4], q1[4], c1[4], a2[4], q2[4], c2[4];   // bf16 pairs, packed as formed
+#pragma unroll
+    for (int e2i = 0; e2i < 4; ++e2i) {
+      float v[2][6];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = 2 * e2i + u;
+        const float G = Gs[8 * s + e];
+        const float g7 = row_bcast<7>(G), g15 = row_bcast<15>(G);   // broadcasts first, selects after
+        const float m = hi ? 0.5f * (g7 + g15) : 0.5f * g7;
+        const float up = fast_exp2(G - m), dn = fast_exp2(m - G);
+        const float ex = fast_exp2(hi ? G - g7 : g7 - G);           // <= 1
+        const float kn = kf[e] * rk, qn = qf[e] * rq;
+        v[u][0] = kn * up;
+        v[u][1] = qn * up;
+        v[u][2] = kn * dn;
+        v[u][3] = hi ? kn * ex : 0.0f;
+        v[u][4] = hi ? qn * ex : 0.0f;
+        v[u][5] = hi ? 0.0f : kn * ex;
+      }
+      a1[e2i] = pack_bf16x2(v[0][0], v[1][0]);
+      q1[e2i] = pack_bf16x2(v[0][1], v[1][1]);
+      c1[e2i] = pack_bf16x2(v[0][2], v[1][2]);
+      a2[e2i] = pack_bf16x2(v[0][3], v[1][3]);
+      q2[e2i] = pack_bf16x2(v[0][4], v[1][4]);
+      c2[e2i] = pack_bf16x2(v[0][5], v[1][5]);
+    }
+    const u32x4 C1 = {c1[0], c1[1], c1[2], c1[3]}, C2 = {c2[0], c2[1], c2[2], c2[3]};
+    aD = mfma_bf16(u32x4{a1[0], a1[1], a1[2], a1[3]}, C1, aD);
+    qD = mfma_bf16(C1, u32x4{q1[0], q1[1], q1[2], q1[3]}, qD);
+    aX = mfma_bf16(u32x4{a2[0], a2[1], a2[2], a2[3]}, C2, aX);
+    qX = mfma_bf16(C2, u32x4{q2[0], q2[1], q2[2], q2[3]}, qX);
+  }
+  // aD[j] = D[4gq + j][lt] (row, column); qD[j] = D[key 4gq + j][query lt]
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool same = (4 * gq + j >= 8) == hi;
+    aD[j] = same ? aD[j] : aX[j];
+    qD[j] = same ? qD[j] : qX[j];
+  }
+}
+
 // Largest sub-chunk gate sum (log2 units) for which the factorised diagonal blocks
 // stay finite: their column factor 2^-Gs is at most 2^118, and a 32-channel MFMA
 // step then sums at most 128 * 2^118 = 2^125 < FLT_MAX.
 constexpr float DIAG_RANGE2 = 118.0f;
 
-// Largest sub-chunk gate sum (log2 units) for the diagonal blocks factorised about each
-// channel's midpoint m = total / 2 instead of the sub-chunk start: the factors 2^(Gs - m)
-// and 2^(m - Gs) then stay within 2^(+-100), finite and (for key or query components
-// above 2^-26) clear of the subnormal range, and every kept entry, a product of the two
-// for i <= r, is at most 1. Entries above the diagonal may overflow; they are discarded
-// by the selects that mask the blocks.
+// Largest gate sum (log2 units) of one 8-token half of a sub-chunk for the split form of
+// its diagonal block (split_diag), whose within-half entries are factorised about each
+// channel's midpoint of that half: the factors then stay within 2^(+-100), finite and
+// (for key or query components above 2^-26) clear of the subnormal range, and every kept
+// entry, a product of the two for i <= r, is at most 1. Entries above the diagonal or
+// across the halves may overflow in that product; the selects that merge and mask the
+// blocks discard them.
 constexpr float DIAG_RANGE2_MID = 200.0f;
 
 // UB = false: the safe gate, g~ in [lower_bound, 0] with lower_bound >= -5, so a
 //             16-token sub-chunk spans at most 80 natural-log units and every diagonal
 //             block is formed from the factorised operands on MFMA.
 // UB = true : the gate without the safe bound. Sub-chunks whose gate sums stay within
-//             DIAG_RANGE2 take the same MFMA path; those within DIAG_RANGE2_MID take it
-//             with the midpoint-referenced factors; the others form their diagonal block
-//             with pair_step (a wave-uniform choice, per sub-chunk).
+//             DIAG_RANGE2 take the same MFMA path; those whose 8-token halves each stay
+//             within DIAG_RANGE2_MID take the split form (split_diag); the others form
+//             their diagonal block with pair_step (a wave-uniform choice, per sub-chunk).
 template <bool UB>
 __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
   __shared__ IntraSmem sm;
@@ -253,7 +325,7 @@ __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
   float Gs[32];   // sub-chunk cumulative gates in log2 units (exp2(Gs) = exp of the natural sums)
   float rq, rk;
   bool slow = false;   // (UB only) this sub-chunk's diagonal block is formed entry by entry
-  bool mid = false;    // (UB only) ... on MFMA, factorised about each channel's midpoint
+  bool split = false;  // (UB only) ... on MFMA, in the split form (split_diag)
   // diagonal gram block of this sub-chunk: D[r][i] = k^_r.k^_i exp(Gs_r - Gs_i) and
   // D[i][r] = k^_i.q^_r exp(Gs_r - Gs_i) in D layout (MFMA path, phase B); on the
   // entry-by-entry path (phase A) aD holds the first transposed, see phase D
@@ -279,13 +351,13 @@ __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) vr[s] = load_row8(p.v + rowoff, s, gq, true);
     }
-    const float braw = bf16_to_f32(p.beta[(size_t)(t0 + (valid ? tok : 0)) * H + h]);
     float dtf[32];
     if (fuse_gate) {
       const float* dt = p.dt_bias + (size_t)h * KD;
 #pragma unroll
       for (int s = 0; s < 4; ++s) ld8f(dt + 32 * s + 4 * gq, &dtf[8 * s]);
     }
+    const float braw = bf16_to_f32(p.beta[(size_t)(t0 + (valid ? tok : 0)) * H + h]);
     if (L < CH && !valid) {   // partial chunk: rows past its end are zero
 #pragma unroll
       for (int s = 0; s < 4; ++s) qraw[s] = kraw[s] = graw[s] = u32x4{0u, 0u, 0u, 0u};
@@ -321,8 +393,20 @@ __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 1; i < 32; ++i) mn = fminf(mn, Gs[i]);
       const float wmn = wave_min(mn);
-      slow = __builtin_amdgcn_readfirstlane(wmn < -DIAG_RANGE2_MID ? 1 : 0) != 0;
-      mid = __builtin_amdgcn_readfirstlane(wmn < -DIAG_RANGE2 ? 1 : 0) != 0 && !slow;
+      slow = __builtin_amdgcn_readfirstlane(wmn < -DIAG_RANGE2 ? 1 : 0) != 0;
+      if (slow) {   // the split form applies when each 8-token half spans at most DIAG_RANGE2_MID
+        // largest gate span of an 8-token half: the lanes at each half's end take the sum 8
+        // lanes back (0 past the row start) minus their own
+        float d2 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const float b8 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(Gs[i]), 0x118, 0xf, 0xf, true));
+          d2 = fmaxf(d2, b8 - Gs[i]);
+        }
+        d2 = (lt & 7) == 7 ? d2 : 0.0f;
+        split = __builtin_amdgcn_readfirstlane(wave_max(d2) <= DIAG_RANGE2_MID ? 1 : 0) != 0;
+        slow = !split;
+      }
     }
     if (lt == 15) {
 #pragma unroll
@@ -377,34 +461,38 @@ __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
     const float GL = t0v + t1v + t2v + t3v;
     const float rA = wa ? t0v : 0.0f, rA1 = wa ? t0v + t1v : t0v;                  // ref_wa, ref_wa+1
     const float rB = wa ? t0v + t1v + t2v : t0v + t1v, rB1 = wa ? GL : t0v + t1v + t2v;   // ref_wa+2, ref_wa+3
-    sm.r.g.exref[wa][c] = fast_exp2(rA);   // the totals are in log2 units
-    sm.r.g.eend[wa][c] = fast_exp2(rA1 - rA);
-    sm.r.g.c2[wa][c] = fast_exp2(GL - rA1);
-    sm.r.g.exref[wa + 2][c] = fast_exp2(rB);
-    sm.r.g.eend[wa + 2][c] = fast_exp2(rB1 - rB);
-    sm.r.g.c2[wa + 2][c] = fast_exp2(GL - rB1);
+    const float eA = fast_exp2(rA1 - rA), eB = fast_exp2(rB1 - rB);   // the totals are in log2 units
+    sm.r.g.eend[wa][c] = eA;
+    sm.r.g.eend[wa + 2][c] = eB;
+    sm.r.g.eend_h[wa][c] = (_Float16)eA;
+    sm.r.g.eend_h[wa + 2][c] = (_Float16)eB;
+    sm.r.g.exref_h[wa][c] = (_Float16)fast_exp2(rA);
+    sm.r.g.exref_h[wa + 2][c] = (_Float16)fast_exp2(rB);
+    sm.r.g.c2_h[wa][c] = (_Float16)fast_exp2(GL - rA1);
+    sm.r.g.c2_h[wa + 2][c] = (_Float16)fast_exp2(GL - rB1);
     if (tid < KD) reinterpret_cast<float*>(rec + OFF_GAML)[c] = fast_exp2(GL);
   }
   lds_barrier();
 
   // ---------------- phase B: operands, diagonal grams, permuted copies -------
+  if (UB && split) split_diag(qraw, kraw, Gs, rq, rk, lt, gq, aD, qD);
   const u32x4 idh0 = perm_operand(lt, gq, 0, 0x3C00u), idh1 = perm_operand(lt, gq, 1, 0x3C00u);
   const int half = (w & 1) * 8;   // byte offset of this sub-chunk's tokens inside a 32-token fragment
   u32x4 Rkh[4], Rqh[4];            // off-diagonal gram rows (fp16), kept for phase D
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    float qf[8], kf[8], exr[8], cc2[8];
+    float qf[8], kf[8];
     unpack8(qraw[s], qf);
     unpack8(kraw[s], kf);
-    ld8f(&sm.r.g.exref[w][32 * s + 4 * gq], exr);
-    ld8f(&sm.r.g.c2[w][32 * s + 4 * gq], cc2);
+    const u32x4 exh = ld8h(&sm.r.g.exref_h[w][32 * s + 4 * gq]);   // exp(ref_w) in fp16
+    const u32x4 c2h = ld8h(&sm.r.g.c2_h[w][32 * s + 4 * gq]);      // exp(G_L - ref_w+1) in fp16
     // exp(sub-chunk total) for the factorised path; (UB only) the total itself for a
-    // sub-chunk past DIAG_RANGE2 (diagonal block entry by entry in phase A, or about the
-    // midpoints), where exp(-G) may be out of fp32 range and exp(end_w - G) is taken directly
-    const bool direct = UB && (slow || mid);
+    // sub-chunk past DIAG_RANGE2 (diagonal block entry by entry in phase A, or in the
+    // split form), where exp(-G) may be out of fp32 range and exp(end_w - G) is taken directly
+    const bool direct = UB && (slow || split);
     float en[8];
     ld8f(direct ? &sm.r.g.tot[w][32 * s + 4 * gq] : &sm.r.g.eend[w][32 * s + 4 * gq], en);
-    float rke[8], rqe[8], cki[8], tk[8], kp[8], kg[8], qg[8];
+    float rke[8], rqe[8], cki[8], tk[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float kn = kf[e] * rk, qn = qf[e] * rq;
@@ -414,32 +502,20 @@ __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
       rqe[e] = qn * ee;
       cki[e] = kn * ie;
       tk[e] = kn * (direct ? fast_exp2(en[e] - Gs[8 * s + e]) : ie * en[e]);   // K^ exp(end_w - G) <= 1
-      kp[e] = tk[e] * cc2[e];                     // K^ exp(G_L - G)   <= 1
-      kg[e] = rke[e] * exr[e];                    // K^ exp(G)         <= 1
-      qg[e] = rqe[e] * exr[e];                    // Q^ exp(G)         <= 1
     }
-    if (UB && mid) {       // the same products with the factors taken about m = total / 2
-      float mk[8], mq[8], mc[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float hm = 0.5f * en[e], up = fast_exp2(Gs[8 * s + e] - hm);
-        mk[e] = kf[e] * rk * up;
-        mq[e] = qf[e] * rq * up;
-        mc[e] = kf[e] * rk * fast_exp2(hm - Gs[8 * s + e]);
-      }
-      const u32x4 rkd = pk_bf16(mk), ckd = pk_bf16(mc), rqd = pk_bf16(mq);
-      aD = mfma_bf16(rkd, ckd, aD);
-      qD = mfma_bf16(ckd, rqd, qD);
-    } else if (!(UB && slow)) {   // diagonal gram blocks from the factorised operands
+    if (!(UB && (slow || split))) {   // diagonal gram blocks from the factorised operands
       const u32x4 rkd = pk_bf16(rke), ckd = pk_bf16(cki), rqd = pk_bf16(rqe);
       aD = mfma_bf16(rkd, ckd, aD);                 // D[r][i] = k^_r.k^_i exp(Gs_r - Gs_i)
       qD = mfma_bf16(ckd, rqd, qD);                 // D[i][r] = k^_i.q^_r exp(Gs_r - Gs_i)
     }
     Rkh[s] = pk_f16(rke);
     Rqh[s] = pk_f16(rqe);
-    if (w < 3) sm.r.g.tk[w][s][l] = pk_f16(tk);
-    *reinterpret_cast<u32x4*>(rec + OFF_QG + ((w * 4 + s) * 64 + l) * 16) = pk_f16(qg);
-    const u32x4 kph = pk_f16(kp), kgh = pk_f16(kg);
+    const u32x4 tkh = pk_f16(tk);
+    if (w < 3) sm.r.g.tk[w][s][l] = tkh;
+    // the operands scaled by per-channel factors <= 1, as packed fp16 products:
+    //   Q^ exp(G) = (Q^ exp(Gs)) exp(ref_w),  K^ exp(G) likewise,  K^ exp(G_L - G) = tk exp(G_L - ref_w+1)
+    *reinterpret_cast<u32x4*>(rec + OFF_QG + ((w * 4 + s) * 64 + l) * 16) = mul_f16x8(Rqh[s], exh);
+    const u32x4 kph = mul_f16x8(tkh, c2h), kgh = mul_f16x8(Rkh[s], exh);
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
       const int ct = 2 * s + par;
@@ -469,9 +545,7 @@ __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
     if (w >= 2) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        float d2[8];
-        ld8f(&sm.r.g.eend[w - 1][32 * s + 4 * gq], d2);   // exp(ref_w - ref_{w-1})
-        const u32x4 dh = pk_f16(d2);
+        const u32x4 dh = ld8h(&sm.r.g.eend_h[w - 1][32 * s + 4 * gq]);   // exp(ref_w - ref_{w-1})
         const u32x4 tb = sm.r.g.tk[w - 2][s][l];
         aO[1] = mfma_f16(mul_f16x8(Rkh[s], dh), tb, aO[1]);
         qO[1] = mfma_f16(tb, mul_f16x8(Rqh[s], dh), qO[1]);
@@ -480,12 +554,8 @@ __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
     if (w >= 3) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        float d2[8], d1[8];
-        ld8f(&sm.r.g.eend[2][32 * s + 4 * gq], d2);
-        ld8f(&sm.r.g.eend[1][32 * s + 4 * gq], d1);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) d2[e] *= d1[e];     // exp(ref_3 - ref_1)
-        const u32x4 dh = pk_f16(d2);
+        const u32x4 dh = mul_f16x8(ld8h(&sm.r.g.eend_h[2][32 * s + 4 * gq]),
+                                   ld8h(&sm.r.g.eend_h[1][32 * s + 4 * gq]));   // exp(ref_3 - ref_1)
         const u32x4 tb = sm.r.g.tk[0][s][l];
         aO[2] = mfma_f16(mul_f16x8(Rkh[s], dh), tb, aO[2]);
         qO[2] = mfma_f16(tb, mul_f16x8(Rqh[s], dh), qO[2]);

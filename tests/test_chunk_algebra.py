@@ -99,30 +99,45 @@ def test_factorised_exponentials_stay_in_fp32_range():
     assert worst < math.log(np.finfo(np.float32).max)
 
 
-def test_midpoint_factorised_diagonal_block():
-    """Unbounded gate, sub-chunk gate sums in [-200, -118) (log2 units): the diagonal 16x16
-    blocks factorised about each channel's midpoint m = total / 2 keep both factors
-    2^(Gs - m) and 2^(m - Gs) within 2^(+-100), and in fp32 give every kept entry (key i <=
-    row r) finite and equal to the direct sum sum_c k_r k_i 2^(Gs_r - Gs_i); entries above
-    the diagonal may overflow, which is why the kernels mask them with selects."""
+def test_split_diagonal_block():
+    """Unbounded gate, sub-chunk gate sums below -118 (log2 units) whose 8-token halves each
+    span at most 200: the diagonal 16x16 block in its split form -- entries within a half
+    from factors about that half's per-channel midpoint (g7 / 2, (g7 + g15) / 2), entries of
+    a second-half row against a first-half column from 2^(Gs - g7) and 2^(g7 - Gs) -- keeps
+    every factor within 2^(+-100) and, computed in fp32 and merged by half, gives every kept
+    entry (key i <= row r) finite and equal to the direct sum sum_c k_r k_i 2^(Gs_r - Gs_i);
+    entries above the diagonal or across the halves of the first product may overflow,
+    which is why the kernels merge and mask with selects."""
     rng = np.random.default_rng(5)
     SUB, K = 16, 128
-    for total in (-119.0, -150.0, -199.0):
-        # per-token log2 decays of one sub-chunk whose most negative channel sums to `total`
+    for h1, h2 in ((-119.0, -5.0), (-150.0, -199.0), (-199.0, -199.0), (-60.0, -190.0)):
+        # per-token log2 decays whose most negative channel sums to h1 over tokens 0-7 and
+        # h2 over tokens 8-15
         raw = rng.exponential(1.0, size=(SUB, K))
-        gates = -raw / raw.sum(0, keepdims=True).max() * (-total)
+        gates = np.empty_like(raw)
+        gates[:8] = -raw[:8] / raw[:8].sum(0, keepdims=True).max() * (-h1)
+        gates[8:] = -raw[8:] / raw[8:].sum(0, keepdims=True).max() * (-h2)
         Gs = np.cumsum(gates, axis=0)                    # [token, channel], <= 0, decreasing
-        assert Gs.min() >= total - 1e-9 and Gs.min() < -118
-        m = 0.5 * Gs[-1]                                 # per-channel midpoint
+        g7, g15 = Gs[7], Gs[15]
+        assert max((-g7).max(), (g7 - g15).max()) <= 200 + 1e-9
+        hi = (np.arange(SUB) >= 8)[:, None]
+        m = np.where(hi, 0.5 * (g7 + g15), 0.5 * g7)    # per-token, per-channel reference
         up, dn = np.exp2(Gs - m), np.exp2(m - Gs)
-        assert np.log2(up).max() <= 100 and np.log2(dn).max() <= 100
+        assert np.abs(np.log2(up)).max() <= 100 and np.abs(np.log2(dn)).max() <= 100
+        ex = np.exp2(np.where(hi, Gs - g7, g7 - Gs))
+        assert ex.max() <= 1.0
         k = rng.standard_normal((SUB, K))
         k /= np.sqrt((k ** 2).sum(1, keepdims=True))
         direct = np.einsum('rc,ic,ric->ri', k, k, np.exp2(Gs[:, None, :] - Gs[None, :, :]))
         with np.errstate(over='ignore', invalid='ignore'):
-            f32 = (k * up).astype(np.float32) @ (k * dn).astype(np.float32).T
+            d1 = (k * up).astype(np.float32) @ (k * dn).astype(np.float32).T
+        rows2 = np.where(hi, k * ex, 0.0).astype(np.float32)
+        cols2 = np.where(hi, 0.0, k * ex).astype(np.float32)
+        d2 = rows2 @ cols2.T
+        same = hi == hi.T                                # row and column in the same half
+        merged = np.where(same, d1, d2)
         keep = np.tril(np.ones((SUB, SUB), bool))
-        assert np.isfinite(f32[keep]).all()
-        np.testing.assert_allclose(f32[keep], direct[keep], rtol=1e-4, atol=1e-6)
-        # the plain factorisation about the sub-chunk start would need 2^-Gs beyond 2^118
+        assert np.isfinite(merged[keep]).all()
+        np.testing.assert_allclose(merged[keep], direct[keep], rtol=1e-4, atol=1e-6)
+        # one reference point for the whole sub-chunk would need 2^-Gs beyond 2^118
         assert -Gs.min() > 118

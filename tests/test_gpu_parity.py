@@ -470,18 +470,18 @@ def test_fusion_switches_off(shape, sw, path):
 # gate without the safe bound (safe_gate off): -exp(A_log) softplus(g + dt_bias), or
 # min(g, 0) unfused. The regimes steer the 16-token gate sums: "mild" keeps every
 # sub-chunk on the factorised MFMA path, "strong" and "unfused" push most sub-chunks
-# past it (entry-by-entry diagonal blocks), "mixed" puts huge and tiny per-channel
+# past it (split-form or entry-by-entry diagonal blocks), "mixed" puts huge and tiny per-channel
 # gates in the same sub-chunks and mixes both kinds of heads, "tiers" gives the heads
-# gate rates 3, 5.5 and 9 (the last H of them), whose 16-token sums put every sub-chunk
-# of a head on one diagonal-block form: factorised from the sub-chunk start, factorised
-# about the channel midpoints, entry by entry.
+# gate rates 3, 9 and 40 (the last H of them), whose 16-token sums put every sub-chunk
+# of a head on one diagonal-block form: factorised from the sub-chunk start, the split
+# form (each 8-token half about its own midpoints), entry by entry.
 def _unbounded_inputs(d, regime):
     d = dict(d)
     H, K = d['dt_bias'].shape
     if regime == "mild":
         d['A_log'] = torch.full((H,), -3.5)
     elif regime == "tiers":
-        d['A_log'] = torch.log(torch.tensor([3.0, 5.5, 9.0][-H:]))
+        d['A_log'] = torch.log(torch.tensor([3.0, 9.0, 40.0][-H:]))
     elif regime == "mixed":
         al = torch.full((H,), math.log(16.0))
         al[0::2] = -3.0
