@@ -32,8 +32,10 @@ fp32 final state). Prints ONE JSON line.
   cpu_baseline the fp64 CPU oracle timed on the host cores over the same
               workload (bounded: see "sample"), with a one-thread figure
 
-Timing: W warm-up steps (default 50: an idle GPU takes some milliseconds to
-raise its clocks, and the first tens of calls run up to 7% slower), then K timed
+Timing: about 50 ms of plain device copies first (--settle-ms; no step of the
+method, reported as clock_settle_ms: an idle GPU takes some milliseconds to
+raise its clocks, and without it the first tens of calls run up to 12% slower),
+then W warm-up steps (default 50), then K timed
 steps between two HIP events on the launch stream, with nothing recorded
 between the calls; the steps alternate between two input sets (distinct
 tensors, the second drawn with the next seed) so that no step finds its inputs
@@ -105,6 +107,30 @@ def copy_calibration(steps):
           flush=True)
 
 
+def settle_clocks(dev, ms):
+    """Keep the GPU busy with plain device copies for about `ms` milliseconds, so that the
+    warm-up and timed steps that follow run at the clocks a busy GPU holds (an idle GPU
+    takes some milliseconds to raise them). Nothing of the method runs here."""
+    import torch
+    if ms <= 0:
+        return 0.0
+    a = torch.empty(64 << 20, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    t = time.perf_counter()
+    while True:
+        for _ in range(8):
+            b.copy_(a)
+        e1.record()
+        e1.synchronize()
+        if e0.elapsed_time(e1) >= ms or time.perf_counter() - t > 5.0:
+            break
+    del a, b
+    return e0.elapsed_time(e1)
+
+
 def cpu_threads():
     n = os.environ.get("OMP_NUM_THREADS")
     if n and n.isdigit():
@@ -136,6 +162,8 @@ def main():
     ap.add_argument("--gate", choices=["safe", "unbounded"], default="safe",
                     help="safe: lower_bound * sigmoid gate (the default); unbounded: the gate without the "
                          "safe bound, -exp(A_log) * softplus(g + dt_bias)")
+    ap.add_argument("--settle-ms", type=float, default=50.0,
+                    help="plain device copies for this long before the warm-up steps (clock settle)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra workload (uniform varlen 8 x 1024) timed after the headline one")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -202,6 +230,7 @@ def measure(widx, args, headline):
                               x['dt_bias'], x['lower_bound'], initial_state=x['initial_state'],
                               final_state=fin, cu_seqlens=x['cu_seqlens'], safe_gate=safe)
 
+    settled_ms = settle_clocks(dev, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -294,6 +323,7 @@ def measure(widx, args, headline):
                    "frac_mfma_bf16": flops / (call_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
     if prof_ms is not None:
         res["path"]["profiled_call_ms"] = prof_ms
+    res["clock_settle_ms"] = settled_ms
     res["kernels"] = kernels
     if headline:
         res["wall_s_timed"] = t_wall
