@@ -24,7 +24,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["fwd", "fwd_recurrent", "workspace_size", "record_bytes", "lib", "KDAError", "status_string", "LIB_PATH",
+__all__ = ["fwd", "fwd_recurrent", "workspace_size", "workspace_min", "record_bytes", "lib", "KDAError", "status_string", "LIB_PATH",
            "profile_start", "profile_stop"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -51,6 +51,8 @@ def _setup(L):
     F = ctypes.c_float
     L.kda_fwd_workspace_size.restype = ctypes.c_size_t
     L.kda_fwd_workspace_size.argtypes = [I64, I64, I64, I64]
+    L.kda_fwd_workspace_min.restype = ctypes.c_size_t
+    L.kda_fwd_workspace_min.argtypes = [I64, I64, I64, I64]
     L.kda_fwd.restype = I
     L.kda_fwd.argtypes = [P, P, P, P, P, F, P, P, P, F, P, I, P, I, P, I64, I64, I64, I64, I64, I64, P,
                           ctypes.c_size_t, P]
@@ -101,6 +103,12 @@ def status_string(code: int) -> str:
 def workspace_size(B: int, T: int, H: int, N: int = 0) -> int:
     """Bytes of workspace kda_fwd needs (N = number of sequences with cu_seqlens, else 0)."""
     return int(lib().kda_fwd_workspace_size(int(B), int(T), int(H), int(N)))
+
+
+def workspace_min(B: int, T: int, H: int, N: int = 0) -> int:
+    """Smallest workspace kda_fwd accepts; fixed-length calls given less than
+    workspace_size run in windows of chunk columns (kda_fwd_workspace_min)."""
+    return int(lib().kda_fwd_workspace_min(int(B), int(T), int(H), int(N)))
 
 
 def record_bytes() -> int:
@@ -191,6 +199,11 @@ def fwd(q, k, v, g, beta, scale: float, out, A_log, dt_bias, lower_bound: float,
     sequence on average) run on the token-recurrent kernel instead, unless
     ``force_chunked`` is set (KDA_PATH_CHUNKED of kda_fwd_ex).
 
+    ``workspace``: a uint8 device tensor (allocated here when None). Fixed-length
+    calls given less than workspace_size (at least workspace_min) run in windows of
+    chunk columns; a workspace below the minimum is rejected by the library
+    (KDAError with KDA_ERR_WORKSPACE).
+
     The three switches select the in-kernel input processing (default) or take
     that input as already processed: g as the log-decay (clamped into
     [lower_bound, 0]; A_log and dt_bias may be None), q and k as given, beta as
@@ -204,11 +217,10 @@ def fwd(q, k, v, g, beta, scale: float, out, A_log, dt_bias, lower_bound: float,
     B, T, H, K, V, N = _prepare(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens,
                                 gate_fused=use_gate_in_kernel)
     L = lib()
-    ws_bytes = workspace_size(B, T, H, N)
     if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
-    elif workspace.numel() * workspace.element_size() < ws_bytes or workspace.device != q.device:
-        raise ValueError(f"workspace must hold {ws_bytes} bytes on {q.device}")
+        workspace = torch.empty(max(workspace_size(B, T, H, N), 1), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device:
+        raise ValueError(f"workspace must be on {q.device}")
     rc = L.kda_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(out), _ptr(A_log),
                       _ptr(dt_bias), float(lower_bound), _ptr(initial_state), _state_code(initial_state),
                       _ptr(final_state), _state_code(final_state), _ptr(cu_seqlens), N, B, T, H, K, V, flags,

@@ -8,6 +8,7 @@
 // [-5, 0]; optional bf16/fp32 states of equal dtype; cu_seqlens requires B = 1.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -98,6 +99,39 @@ bool make_layout(int64_t B, int64_t T, int64_t H, int64_t N, bool varlen, Layout
 }
 
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Fixed-length calls given less workspace than the full layout run in windows of chunk
+// columns: launch pair w covers chunks jb = w * nc_win .. jb + nc_win - 1 of every row
+// (the intra-chunk kernel, then the plain state chain), so the records of nc_win chunks
+// per row are held at a time. A row's state crosses from one window to the next in fp32:
+// in final_state itself when that is fp32 (each workgroup reads its slice of it when it
+// starts and writes the slice when it ends), otherwise in a carry region of the
+// workspace. Every window runs the same per-chunk arithmetic as one full launch and the
+// carried state is exact, so the results are bit-identical to an unwindowed call; the
+// chain takes the same number of steps per row, split over the windows.
+constexpr size_t WORKSPACE_TARGET = (size_t)1 << 30;   // kda_fwd_workspace_size's bound where windows apply
+struct Windows {
+  int64_t count = 0, nc_win = 0;
+  size_t rec = 0, carry = 0, total = 0;
+  bool own_carry = false;
+};
+size_t carry_bytes(int64_t B, int64_t H) { return align_up((size_t)B * H * kda::VD * kda::KD * sizeof(float)); }
+size_t column_bytes(int64_t B, int64_t H) { return (size_t)B * H * kda::REC_BYTES; }   // a multiple of 256
+static_assert(kda::REC_BYTES % ALIGN == 0, "records keep the workspace alignment");
+bool plan_windows(int64_t B, int64_t T, int64_t H, bool final_fp32, size_t bytes, Windows& W) {
+  const int64_t nc_row = (T + kda::CH - 1) / kda::CH;
+  if (nc_row < 1) return false;
+  W.own_carry = !final_fp32;
+  W.carry = W.own_carry ? carry_bytes(B, H) : 0;
+  const size_t col = column_bytes(B, H);
+  if (bytes < W.carry + col) return false;
+  const int64_t fit = (int64_t)((bytes - W.carry) / col);
+  W.count = (nc_row + fit - 1) / fit;                 // fewest windows, then balanced widths
+  W.nc_win = (nc_row + W.count - 1) / W.count;
+  W.rec = (size_t)W.nc_win * col;
+  W.total = W.rec + W.carry;
+  return true;
+}
 
 // Calls that kda_fwd / kda_fwd_ex hand to the token-recurrent kernel: fixed-length rows of
 // at most REC_MAX_T tokens, or varlen batches of at most REC_MAX_AVG tokens per sequence on
@@ -251,7 +285,21 @@ extern "C" {
 size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N) {
   Layout L;
   if (!make_layout(B, T, H, N, N > 0, L)) return 0;
+  // fixed-length calls on the plain chain: windows of chunk columns within WORKSPACE_TARGET
+  // (at T = 32768, B = 4, H = 64 the full 9.5 GiB and 1 GiB in ten windows take the same time)
+  Windows W;
+  if (N == 0 && L.nseg == 1 && L.total > WORKSPACE_TARGET &&
+      plan_windows(B, T, H, false, WORKSPACE_TARGET, W) && W.total < L.total)
+    return W.total;
   return L.total;
+}
+
+size_t kda_fwd_workspace_min(int64_t B, int64_t T, int64_t H, int64_t N) {
+  Layout L;
+  if (!make_layout(B, T, H, N, N > 0, L)) return 0;
+  if (N > 0 || L.total == 0) return L.total;
+  const size_t one = carry_bytes(B, H) + column_bytes(B, H);   // one chunk column and a carry
+  return one < L.total ? one : L.total;
 }
 
 int kda_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale, void* out,
@@ -274,8 +322,12 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
   const bool varlen = cu_seqlens != nullptr;
   Layout L;
   if (!make_layout(B, T, H, varlen ? N : 0, varlen, L)) return KDA_ERR_SHAPE;
+  Windows W;   // W.count > 0: the call runs in windows of chunk columns (fixed length only)
   if (L.total > 0) {
-    if (!workspace || workspace_bytes < L.total) return KDA_ERR_WORKSPACE;
+    if (!workspace) return KDA_ERR_WORKSPACE;
+    if (workspace_bytes < L.total &&
+        (varlen || !plan_windows(B, T, H, final_dtype == KDA_STATE_FP32, workspace_bytes, W)))
+      return KDA_ERR_WORKSPACE;
     if (!aligned(workspace, ALIGN)) return KDA_ERR_ALIGN;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -303,6 +355,32 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
   p.map.max_chunks = (int32_t)L.max_chunks;
   p.map.nseq = (int32_t)(varlen ? N : B);
   p.map.nc_row = (int32_t)((T + kda::CH - 1) / kda::CH);
+  p.map.jb = 0;
+  p.map.nc_win = p.map.nc_row;
+  if (W.count > 0) {   // windows of chunk columns (no per-kernel timing for these calls)
+    if (env_flag("KDA_LOG"))
+      std::fprintf(stderr, "[kda] fwd B=%lld T=%lld H=%lld windows=%lld x %lld chunks workspace=%zu of %zu\n",
+                   (long long)B, (long long)T, (long long)H, (long long)W.count, (long long)W.nc_win, W.total,
+                   L.total);
+    p.rec = ws;
+    void* carry = W.own_carry ? static_cast<void*>(ws + W.rec) : final_state;
+    hipError_t e = hipSuccess;
+    for (int64_t w = 0; w < W.count && e == hipSuccess; ++w) {
+      const int64_t jb = w * W.nc_win;
+      const int64_t width = std::min<int64_t>(W.nc_win, p.map.nc_row - jb);
+      p.map.jb = (int32_t)jb;
+      p.map.nc_win = (int32_t)width;
+      p.map.max_chunks = (int32_t)(B * width);
+      p.init_state = w == 0 ? initial_state : carry;
+      p.init_dtype = w == 0 ? initial_dtype : KDA_STATE_FP32;
+      const bool last = w + 1 == W.count;
+      p.final_state = last ? final_state : carry;
+      p.final_dtype = last ? final_dtype : KDA_STATE_FP32;
+      e = kda::launch_intra(p, st);
+      if (e == hipSuccess) e = kda::launch_chain(p, st);
+    }
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  }
   // segment-parallel chain: the layout's segment count, or fewer with KDA_CHAIN_SEGMENTS
   int64_t nseg = L.nseg;
   if (const char* e = std::getenv("KDA_CHAIN_SEGMENTS")) {

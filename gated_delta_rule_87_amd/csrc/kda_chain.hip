@@ -151,10 +151,10 @@ __global__ __launch_bounds__((3 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
       t0 = __builtin_amdgcn_readfirstlane(sp.x);
       length = __builtin_amdgcn_readfirstlane(sp.y);
     } else {
-      first = row * p.map.nc_row;
-      count = p.map.nc_row;
-      t0 = row * p.map.T;
-      length = p.map.T;
+      first = row * p.map.nc_win;
+      count = p.map.nc_win;
+      t0 = row * p.map.T + p.map.jb * CH;
+      length = p.map.T - p.map.jb * CH;
     }
     const int sc = (count + p.seg.nseg - 1) / p.seg.nseg;   // chunks per segment of this row
     const int cs = sg * sc;
@@ -170,10 +170,10 @@ __global__ __launch_bounds__((3 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
     tok0 = __builtin_amdgcn_readfirstlane(sp.x);
     len = __builtin_amdgcn_readfirstlane(sp.y);
   } else {
-    c0 = n * p.map.nc_row;
-    nc = p.map.nc_row;
-    tok0 = n * p.map.T;
-    len = p.map.T;
+    c0 = n * p.map.nc_win;   // this launch's chunks jb .. jb + nc_win - 1 of row n
+    nc = p.map.nc_win;
+    tok0 = n * p.map.T + p.map.jb * CH;
+    len = p.map.T - p.map.jb * CH;
   }
 
   if (w == 3 * NW) {

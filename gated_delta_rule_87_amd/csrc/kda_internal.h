@@ -10,8 +10,10 @@ namespace kda {
 // switches (same values as the KDA_FUSE_* / KDA_GATE_UNBOUNDED constants of the public header)
 constexpr uint32_t FUSE_GATE = 1, FUSE_QK_L2NORM = 2, FUSE_BETA_SIGMOID = 4, GATE_UNBOUNDED = 8;
 
-// Where a chunk's tokens are: fixed-length rows (B rows of T tokens, chunk i is
-// row i / nc_row, piece i % nc_row) or the varlen tables built on the device.
+// Where a chunk's tokens are: fixed-length rows (B rows of T tokens) or the varlen
+// tables built on the device. A fixed-length launch covers chunks jb .. jb + nc_win - 1
+// of every row (all of them unless the workspace holds fewer: see the windowed calls of
+// kda_fwd_ex); its slot i is row i / nc_win, chunk jb + i % nc_win of that row.
 struct ChunkMap {
   const int2* chunk_tab;   // varlen: [max_chunks] {t0, len}; len = 0 -> unused slot
   const int2* seq_tab;     // varlen: [N] {first chunk, number of chunks}
@@ -19,6 +21,8 @@ struct ChunkMap {
   const int32_t* seq_order;  // varlen: [N] sequences by chunk count, longest first
   int32_t T;               // tokens per row (fixed) / packed total (varlen)
   int32_t nc_row;          // chunks per row (fixed)
+  int32_t jb;              // first chunk of each row in this launch (fixed; 0 for varlen)
+  int32_t nc_win;          // chunks of each row in this launch (fixed; nc_row unless windowed)
   int32_t max_chunks;      // number of chunk slots
   int32_t nseq;            // sequences (B or N)
 };

@@ -303,7 +303,7 @@ __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
     t0 = e.x;
     L = e.y;
   } else {
-    const int row = ci / p.map.nc_row, j = ci - row * p.map.nc_row;
+    const int row = ci / p.map.nc_win, j = p.map.jb + (ci - row * p.map.nc_win);
     t0 = row * p.map.T + j * CH;
     L = min(CH, p.map.T - j * CH);
   }

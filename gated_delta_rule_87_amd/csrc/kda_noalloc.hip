@@ -11,8 +11,8 @@
 //
 // Nothing in the array needs clearing between calls: within one call every word the
 // kernels read is written first (the scheduler's tables, the intra-chunk records of
-// every used chunk slot, the segment maps and states), so the previous call's contents
-// never matter. All calls on one GPU share its array, so calls that overlap on one
+// every used chunk slot, the segment maps and states, a windowed call's carried state),
+// so the previous call's contents never matter. All calls on one GPU share its array, so calls that overlap on one
 // device (several streams, several host threads) race and must be serialised by the
 // caller.
 #include <hip/hip_runtime.h>
@@ -59,8 +59,9 @@ int kda_fwd_noalloc(const void* q, const void* k, const void* v, const void* g, 
                     const int64_t* cu_seqlens, int64_t N, int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
                     uint32_t flags, void* stream) {
   // sizes the workspace layout rejects, and every other argument error, are reported by
-  // kda_fwd_ex itself, before anything is launched
-  const size_t need = kda_fwd_workspace_size(B, T, H, cu_seqlens ? N : 0);
+  // kda_fwd_ex itself, before anything is launched. A fixed-length call whose full
+  // workspace exceeds the array runs in windows of chunk columns that fit it.
+  const size_t need = kda_fwd_workspace_min(B, T, H, cu_seqlens ? N : 0);
   if (need > CAPACITY) return KDA_ERR_CAPACITY;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return KDA_ERR_HIP;

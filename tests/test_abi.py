@@ -32,7 +32,7 @@ def test_header_symbols_exported():
     assert {"kda_fwd", "kda_fwd_recurrent", "kda_fwd_workspace_size", "kda_status_string",
             "kda_version", "kda_profile_start", "kda_profile_stop", "kda_profile_kernel_count",
             "kda_profile_kernel_name", "kda_fwd_ex", "kda_fwd_recurrent_ex", "kda_fwd_noalloc",
-            "kda_noalloc_capacity"} <= set(names)
+            "kda_noalloc_capacity", "kda_fwd_workspace_min"} <= set(names)
     L = ctypes.CDLL(kda.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"libkda.so does not export {n}"
@@ -51,7 +51,12 @@ def test_workspace_size():
     rec = 76288                         # bytes per (64-token chunk, head)
     al = lambda x: (x + 255) // 256 * 256
     assert kda.workspace_size(1, 8192, 64) == al(128 * 64 * rec)
-    assert kda.workspace_size(4, 32768, 64) == al(4 * 512 * 64 * rec)
+    # beyond 1 GiB on the plain chain: windows of chunk columns within 1 GiB (fp32 carry of
+    # 64 KiB per (row, head), then the fewest windows that fit, with balanced widths)
+    carry, col = al(4 * 64 * 128 * 128 * 4), 4 * 64 * rec
+    fit = ((1 << 30) - carry) // col
+    count = -(-512 // fit)
+    assert kda.workspace_size(4, 32768, 64) == carry + -(-512 // count) * col <= 1 << 30
     assert kda.workspace_size(1, 100, 2) == al(2 * 2 * rec)             # ceil(100/64) = 2
     # varlen: floor(T/64) + N chunk slots, plus the tables
     ws = kda.workspace_size(1, 8192, 64, 8)
@@ -121,8 +126,28 @@ def test_validation_errors(fn):
 def test_workspace_errors():
     need = kda.workspace_size(1, 64, 2)
     assert call(ws=None, wsb=0) == EWS
-    assert call(ws=FAKE, wsb=need - 1) == EWS
+    assert call(ws=FAKE, wsb=need - 1) == EWS      # one chunk per row: no smaller windowed form
     assert call(ws=FAKE + 16, wsb=need) == EALIGN
+    # fixed length: below the windowed minimum is rejected before anything is launched
+    mn = kda.workspace_min(2, 1000, 4)
+    assert call(B=2, T=1000, H=4, ws=FAKE, wsb=mn - 1) == EWS
+    # varlen: the full size is the minimum
+    full = kda.workspace_size(1, 1000, 4, 3)
+    assert kda.workspace_min(1, 1000, 4, 3) == full
+    assert call(T=1000, H=4, cu=FAKE, N=3, ws=FAKE, wsb=full - 1) == EWS
+
+
+def test_workspace_min():
+    """One chunk column (B * H records) and an fp32 carry of 64 KiB per (row, head), or the
+    full size when that is smaller; varlen calls: the full size."""
+    rec = kda.record_bytes()
+    al = lambda x: (x + 255) // 256 * 256
+    for B, T, H in [(1, 8192, 64), (4, 32768, 64), (2, 1000, 4), (3, 200, 1)]:
+        full = kda.workspace_size(B, T, H)
+        assert kda.workspace_min(B, T, H) == min(full, al(B * H * 128 * 128 * 4) + B * H * rec)
+    assert kda.workspace_min(1, 64, 2) == kda.workspace_size(1, 64, 2)    # one chunk per row
+    assert kda.workspace_min(1, 8192, 64, 8) == kda.workspace_size(1, 8192, 64, 8)
+    assert kda.workspace_min(1, 0, 4) == 0 and kda.workspace_min(0, 10, 4) == 0
 
 
 def test_python_wrapper_rejects_cpu_tensors():
@@ -231,13 +256,16 @@ def test_workspace_size_with_segmented_chain():
 
 
 def test_noalloc_capacity_check_on_host():
-    """kda_fwd_noalloc rejects a call whose workspace exceeds its fixed array before any
-    HIP call (KDA_ERR_CAPACITY); the capacity is the header's 256 MiB."""
+    """kda_fwd_noalloc rejects, before any HIP call (KDA_ERR_CAPACITY), a call whose
+    smallest workspace (kda_fwd_workspace_min) exceeds its fixed array: varlen calls
+    beyond the array, fixed-length calls whose single chunk column and carry do not fit.
+    The capacity is the header's 256 MiB."""
     L = kda.lib()
     cap = L.kda_noalloc_capacity()
     assert cap == 256 << 20
-    assert kda.workspace_size(1, 8192, 64) > cap >= kda.workspace_size(1, 4096, 54)
+    assert kda.workspace_size(1, 8192, 64, 4) > cap >= kda.workspace_size(1, 4096, 54, 1)
+    assert kda.workspace_min(16, 8192, 128) > cap >= kda.workspace_min(1, 8192, 64)
     P = ctypes.c_void_p
-    args = [P(FAKE)] * 5 + [0.088, P(FAKE), P(FAKE), P(FAKE), -5.0, None, 0, None, 0, None, 0]
-    assert L.kda_fwd_noalloc(*args, 1, 8192, 64, 128, 128, 7, None) == ECAP
-    assert L.kda_fwd_noalloc(*args, 2, 32768, 8, 128, 128, 7, None) == ECAP
+    args = [P(FAKE)] * 5 + [0.088, P(FAKE), P(FAKE), P(FAKE), -5.0, None, 0, None, 0]
+    assert L.kda_fwd_noalloc(*args, P(FAKE), 4, 1, 8192, 64, 128, 128, 7, None) == ECAP    # varlen
+    assert L.kda_fwd_noalloc(*args, None, 0, 16, 8192, 128, 128, 128, 7, None) == ECAP    # B * H too large

@@ -1,7 +1,8 @@
 """kda_fwd_noalloc (workspace in the library's fixed device array) against kda_fwd_ex
 with a caller workspace, through the C ABI: bit-identical results on consecutive calls,
 the later ones smaller than the first (the array keeps the earlier call's contents,
-which must not matter), and the host-side rejection of calls beyond the capacity."""
+which must not matter), fixed-length calls beyond the capacity (run in windows of chunk
+columns), and the host-side rejection of calls whose smallest workspace exceeds it."""
 import ctypes
 
 import numpy as np
@@ -95,17 +96,40 @@ def test_noalloc_matches_workspace_entry(order):
             assert frel <= (2e-3 if w.final == 'fp32' else 5e-3)
 
 
-def test_noalloc_rejects_beyond_capacity():
-    """T = 8192, H = 64 needs 625 MB of workspace: rejected on the host, nothing written."""
+def test_noalloc_windowed_beyond_capacity():
+    """T = 8192, H = 64 needs 625 MB of workspace for one launch pair: the no-alloc entry
+    runs it in windows of chunk columns within its 256 MiB, bit-identical to kda_fwd_ex
+    with the full workspace; then a smaller call through the same array."""
     device = torch.device("cuda:0")
-    w = kda_inputs.custom(B=1, T=8192, H=64)
-    assert kda.workspace_size(1, 8192, 64, 0) > CAPACITY
+    for c in (dict(B=1, T=8192, H=64, state="fp32"), dict(B=4, T=8192, H=16, state="bf16", final="bf16")):
+        w = kda_inputs.custom(**c)
+        full = kda.workspace_size(w.B, w.T, w.H, 0)
+        assert kda.workspace_min(w.B, w.T, w.H, 0) <= CAPACITY
+        say(f"no-alloc windowed call: {c} (full workspace {full} bytes)")
+        d = kda_inputs.make_inputs(w)
+        x = {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+        o1, f1 = _run("noalloc", w, x)
+        o2, f2 = _run("ex", w, x)
+        assert torch.isfinite(o1.float()).all() and torch.isfinite(f1.float()).all()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), "out differs"
+        assert torch.equal(f1.view(torch.int16) if f1.dtype == torch.bfloat16 else f1.view(torch.int32),
+                           f2.view(torch.int16) if f2.dtype == torch.bfloat16 else f2.view(torch.int32)), \
+            "final differs"
+
+
+def test_noalloc_rejects_beyond_capacity():
+    """Two varlen sequences of 4096 tokens at H = 64 need 635 MB of workspace, and varlen
+    calls do not run in windows: rejected on the host, nothing written."""
+    device = torch.device("cuda:0")
+    w = kda_inputs.custom(lengths=[4096, 4096], H=64)
+    assert kda.workspace_min(1, 8192, 64, 2) > CAPACITY
     z = torch.zeros(1, 8192, 64, 128, dtype=torch.bfloat16, device=device)
     x = dict(q=z, k=z, v=z, g=z, beta=torch.zeros(1, 8192, 64, dtype=torch.bfloat16, device=device),
              A_log=torch.zeros(64, device=device), dt_bias=torch.zeros(64, 128, device=device), scale=0.1,
-             lower_bound=-5.0, initial_state=None, cu_seqlens=None)
+             lower_bound=-5.0, initial_state=None,
+             cu_seqlens=torch.tensor([0, 4096, 8192], dtype=torch.int64, device=device))
     out = torch.full_like(z, float('nan'))
-    fin = torch.full((1, 64, 128, 128), float('nan'), device=device)
+    fin = torch.full((2, 64, 128, 128), float('nan'), device=device)
     rc = _call("noalloc", w, x, out, fin)
     assert rc == KDA_ERR_CAPACITY, kda.status_string(rc)
     torch.cuda.synchronize()
