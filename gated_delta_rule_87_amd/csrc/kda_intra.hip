@@ -160,26 +160,39 @@ __device__ __forceinline__ float row_bcast(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + I, 0xf, 0xf, false));
 }
 
-// Diagonal 16x16 gram blocks of one sub-chunk taken entry by entry, for gates of any
-// size. Lane (gq, r) holds token r and 8 channels of k^, q^ and the per-token decays
-// alpha = exp(g~) (log2 units folded in); for every token i of the sub-chunk it adds
-//   PA[i] += k^_r . k^_i E,   PQ[i] += q^_r . k^_i E,   E = exp(G_r - G_i) (i <= r)
-// over its channels. E is a running product of the decays of tokens i+1..r, restarted
-// at 1 where i >= r, so it never overflows; entries i > r are masked by the caller.
+// Largest gate sum (log2 units) of one 8-token half of a sub-chunk for the split form of
+// its diagonal block (split_diag), whose within-half entries are factorised about each
+// channel's midpoint of that half: the factors then stay within 2^(+-100), finite and
+// (for key or query components above 2^-26) clear of the subnormal range, and every kept
+// entry, a product of the two for i <= r, is at most 1. Entries above the diagonal or
+// across the halves may overflow in that product; the selects that merge and mask the
+// blocks discard them.
+constexpr float DIAG_RANGE2_MID = 200.0f;
+
+// Diagonal 16x16 gram block entries of one sub-chunk over one channel per lane, for
+// gates of any size. Lane (gq, r) holds token r's k^, q^ and decay alpha = exp(g~) (log2
+// units folded in) of one channel; for every token i of the sub-chunk it adds
+//   PA[i] += k^_r . k^_i E,   PQ[i] += q^_r . k^_i E,   E = exp(G_r - G_i) (i <= r).
+// E is a running product of the decays of tokens i+1..r, restarted at 1 where i >= r, so
+// it never overflows; entries i > r are masked by the caller. It serves the channels that
+// the split form leaves out (split_diag<true>).
 template <int I>
-__device__ __forceinline__ void pair_step(const float* kn, const float* qn, const float* al, int lt, float* E,
-                                          float* PA, float* PQ) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    if constexpr (I < 15) {   // broadcast first: a cross-lane read must not sit under a lane condition
-      const float a = row_bcast<I + 1>(al[e]);
-      E[e] = (I >= lt) ? 1.0f : E[e] * a;
-    }
-    const float kb = row_bcast<I>(kn[e]) * E[e];
-    PA[I] = fmaf(kn[e], kb, PA[I]);
-    PQ[I] = fmaf(qn[e], kb, PQ[I]);
+__device__ __forceinline__ void pair_step1(float kn, float qn, float al, int lt, float& E, float* PA, float* PQ) {
+  if constexpr (I < 15) {   // broadcast first: a cross-lane read must not sit under a lane condition
+    const float a = row_bcast<I + 1>(al);
+    E = (I >= lt) ? 1.0f : E * a;
   }
-  if constexpr (I > 0) pair_step<I - 1>(kn, qn, al, lt, E, PA, PQ);
+  const float kb = row_bcast<I>(kn) * E;
+  PA[I] = fmaf(kn, kb, PA[I]);
+  PQ[I] = fmaf(qn, kb, PQ[I]);
+  if constexpr (I > 0) pair_step1<I - 1>(kn, qn, al, lt, E, PA, PQ);
+}
+
+// A channel of one sub-chunk that the split form cannot take: an 8-token half of its gate
+// sum spans more than DIAG_RANGE2_MID (g7, g15: the channel's cumulative sums at tokens 7
+// and 15, in log2 units). Both users evaluate it on the same values, so they agree.
+__device__ __forceinline__ bool split_excluded(float g7, float g15) {
+  return fmaxf(-g7, g7 - g15) > DIAG_RANGE2_MID;
 }
 
 // Sums of 16 per-lane values over the four lane groups {l, l^16, l^32, l^48}, leaving
@@ -215,6 +228,9 @@ __device__ __forceinline__ f32x4 reduce_scatter16(const float* P) {
 // half are zero there); the entries are merged by half here, and the caller masks those
 // above the diagonal. Lane (gq, lt) holds token lt and the 32 channels of kraw / qraw /
 // Gs (log2 units).
+// MASK: leave out the channels split_excluded() names (their factors may overflow; the
+// caller adds them entry by entry).
+template <bool MASK>
 __device__ __forceinline__ void split_diag(const u32x4* qraw, const u32x4* kraw, const float* Gs, float rq, float rk,
                                            int lt, int gq, f32x4& aD, f32x4& qD) {
   const bool hi = lt >= 8;
@@ -243,6 +259,11 @@ __device__ __forceinline__ void split_diag(const u32x4* qraw, const u32x4* kraw,
         v[u][3] = hi ? kn * ex : 0.0f;
         v[u][4] = hi ? qn * ex : 0.0f;
         v[u][5] = hi ? 0.0f : kn * ex;
+        if constexpr (MASK) {
+          const bool out = split_excluded(g7, g15);
+#pragma unroll
+          for (int c = 0; c < 6; ++c) v[u][c] = out ? 0.0f : v[u][c];
+        }
       }
       a1[e2i] = pack_bf16x2(v[0][0], v[1][0]);
       q1[e2i] = pack_bf16x2(v[0][1], v[1][1]);
@@ -271,22 +292,14 @@ __device__ __forceinline__ void split_diag(const u32x4* qraw, const u32x4* kraw,
 // step then sums at most 128 * 2^118 = 2^125 < FLT_MAX.
 constexpr float DIAG_RANGE2 = 118.0f;
 
-// Largest gate sum (log2 units) of one 8-token half of a sub-chunk for the split form of
-// its diagonal block (split_diag), whose within-half entries are factorised about each
-// channel's midpoint of that half: the factors then stay within 2^(+-100), finite and
-// (for key or query components above 2^-26) clear of the subnormal range, and every kept
-// entry, a product of the two for i <= r, is at most 1. Entries above the diagonal or
-// across the halves may overflow in that product; the selects that merge and mask the
-// blocks discard them.
-constexpr float DIAG_RANGE2_MID = 200.0f;
-
 // UB = false: the safe gate, g~ in [lower_bound, 0] with lower_bound >= -5, so a
 //             16-token sub-chunk spans at most 80 natural-log units and every diagonal
 //             block is formed from the factorised operands on MFMA.
 // UB = true : the gate without the safe bound. Sub-chunks whose gate sums stay within
 //             DIAG_RANGE2 take the same MFMA path; those whose 8-token halves each stay
-//             within DIAG_RANGE2_MID take the split form (split_diag); the others form
-//             their diagonal block with pair_step (a wave-uniform choice, per sub-chunk).
+//             within DIAG_RANGE2_MID take the split form (split_diag); in the others the
+//             split form takes the channels within that range and pair_step1 the rest,
+//             entry by entry (wave-uniform choices, per sub-chunk and channel slot).
 template <bool UB>
 __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
   __shared__ IntraSmem sm;
@@ -426,27 +439,32 @@ __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
     rk = fuse_norm ? rsqrtf(ssk + 1e-6f) : 1.0f;
     if (gq == 0) sm.beta[tok] = valid ? ((p.flags & FUSE_BETA_SIGMOID) ? sigmoidf_fast(braw) : braw) : 0.0f;
     if (UB && slow) {
+      // the channels the split form leaves out (split_excluded), entry by entry; a channel
+      // slot (s, e) holds one channel per lane group and is skipped when none of its four
+      // channels is excluded (a wave-uniform test)
       float PA[16], PQ[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) PA[i] = PQ[i] = 0.0f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        float qf[8], kf[8], kn[8], qn[8], al[8], E[8];
+        float qf[8], kf[8];
         unpack8(qraw[s], qf);
         unpack8(kraw[s], kf);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          kn[e] = kf[e] * rk;
-          qn[e] = qf[e] * rq;
+          const float G = Gs[8 * s + e];
           // this token's decay: the step of the cumulative sum from the previous token
-          const float prev = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(Gs[8 * s + e]), 0x111, 0xf, 0xf, true));
-          al[e] = fast_exp2(Gs[8 * s + e] - prev);
-          E[e] = 1.0f;
+          const float prev = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(G), 0x111, 0xf, 0xf, true));
+          const float g7 = row_bcast<7>(G), g15 = row_bcast<15>(G);
+          const bool out = split_excluded(g7, g15);
+          if (__builtin_amdgcn_ballot_w64(out) != 0) {
+            float E = 1.0f;
+            pair_step1<15>(out ? kf[e] * rk : 0.0f, out ? qf[e] * rq : 0.0f, fast_exp2(G - prev), lt, E, PA, PQ);
+          }
         }
-        pair_step<15>(kn, qn, al, lt, E, PA, PQ);
       }
       // lane (gq, r) now holds, for columns i = 4gq + j: gram row r (aD) and Aqk of
-      // query r, key i (qD, already the MFMA layout)
+      // query r, key i (qD, already the MFMA layout), over the excluded channels
       aD = reduce_scatter16(PA);
       qD = reduce_scatter16(PQ);
     }
@@ -475,7 +493,13 @@ __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
   lds_barrier();
 
   // ---------------- phase B: operands, diagonal grams, permuted copies -------
-  if (UB && split) split_diag(qraw, kraw, Gs, rq, rk, lt, gq, aD, qD);
+  f32x4 aS = {0, 0, 0, 0};   // (UB, slow sub-chunk) gram block over the channels of the split form
+  if (UB && split) split_diag<false>(qraw, kraw, Gs, rq, rk, lt, gq, aD, qD);
+  if (UB && slow) {
+    f32x4 qS = {0, 0, 0, 0};
+    split_diag<true>(qraw, kraw, Gs, rq, rk, lt, gq, aS, qS);
+    qD += qS;
+  }
   const u32x4 idh0 = perm_operand(lt, gq, 0, 0x3C00u), idh1 = perm_operand(lt, gq, 1, 0x3C00u);
   const int half = (w & 1) * 8;   // byte offset of this sub-chunk's tokens inside a 32-token fragment
   u32x4 Rkh[4], Rqh[4];            // off-diagonal gram rows (fp16), kept for phase D
@@ -564,10 +588,17 @@ __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
     lds_barrier();   // every wave is past its reads of the gram fragments and constants: A may overwrite them
     // rows r = 16w + 4gq + j, columns i = 16b + lt
     const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.beta[16 * w + 4 * gq]);
-    if (UB && slow) {   // aD[j] = gram[lt][4gq + j]
+    if (UB && slow) {   // aS[j] = gram[4gq + j][lt] (split-form channels), aD[j] = gram[lt][4gq + j] (the rest)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * gq + j;
+        sm.r.A[16 * w + r][16 * w + lt] = (r > lt) ? br[j] * aS[j] : 0.0f;
+      }
+      // then the excluded channels' part, added by the same wave (its LDS accesses stay in order)
       const float b = sm.beta[16 * w + lt];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sm.r.A[16 * w + lt][16 * w + 4 * gq + j] = (lt > 4 * gq + j) ? b * aD[j] : 0.0f;
+      for (int j = 0; j < 4; ++j)
+        if (lt > 4 * gq + j) sm.r.A[16 * w + lt][16 * w + 4 * gq + j] += b * aD[j];
     } else {            // aD[j] = gram[4gq + j][lt]
 #pragma unroll
       for (int j = 0; j < 4; ++j) {

@@ -99,6 +99,52 @@ def test_factorised_exponentials_stay_in_fp32_range():
     assert worst < math.log(np.finfo(np.float32).max)
 
 
+def test_split_diagonal_block_with_excluded_channels():
+    """Unbounded gate, a sub-chunk in which some channels' 8-token halves span more than 200
+    (log2 units): the split form takes the other channels (the excluded ones' factors, which
+    may overflow, are zeroed by selects after they are formed) and the excluded channels'
+    entries are summed token pair by token pair from running products of the per-token
+    decays (each at most 1). In fp32, the two parts added give every kept entry (key i <= row
+    r) finite and equal to the direct sum sum_c k_r k_i 2^(Gs_r - Gs_i)."""
+    rng = np.random.default_rng(9)
+    SUB, K = 16, 128
+    for frac, span in ((0.07, 400.0), (0.3, 900.0), (1.0, 250.0)):
+        raw = rng.exponential(1.0, size=(SUB, K))
+        gates = -raw / raw[:8].sum(0, keepdims=True).max() * 150.0        # halves within 200 ...
+        bad_ch = rng.random(K) < frac
+        gates[:, bad_ch] *= span / 150.0                                   # ... except these channels
+        Gs = np.cumsum(gates, axis=0)
+        g7, g15 = Gs[7], Gs[15]
+        excluded = np.maximum(-g7, g7 - g15) > 200
+        assert excluded.any() and not excluded[~bad_ch].any()
+        hi = (np.arange(SUB) >= 8)[:, None]
+        k = rng.standard_normal((SUB, K))
+        k /= np.sqrt((k ** 2).sum(1, keepdims=True))
+        with np.errstate(over='ignore', invalid='ignore'):
+            m = np.where(hi, 0.5 * (g7 + g15), 0.5 * g7)
+            up, dn = np.exp2(Gs - m), np.exp2(m - Gs)
+            ex = np.exp2(np.where(hi, Gs - g7, g7 - Gs))
+            zero = lambda x: np.where(excluded[None, :], 0.0, x).astype(np.float32)
+            d1 = zero(k * up) @ zero(k * dn).T
+            d2 = zero(np.where(hi, k * ex, 0.0)) @ zero(np.where(hi, 0.0, k * ex)).T
+        merged = np.where(hi == hi.T, d1, d2)
+        # the excluded channels, entry by entry: E(r, i) = prod of decays of tokens i+1..r
+        al = np.exp2(np.diff(np.vstack([np.zeros((1, K)), Gs]), axis=0)).astype(np.float32)
+        ks = np.where(excluded[None, :], k, 0.0).astype(np.float32)
+        pair = np.zeros((SUB, SUB), np.float32)
+        for r in range(SUB):
+            E = np.ones(K, np.float32)
+            for i in range(r, -1, -1):
+                if i < r:
+                    E = E * al[i + 1]
+                pair[r, i] = np.float32((ks[r] * ks[i] * E).sum(dtype=np.float32))
+        total = merged + pair
+        direct = np.einsum('rc,ic,ric->ri', k, k, np.exp2(np.minimum(Gs[:, None, :] - Gs[None, :, :], 0.0)))
+        keep = np.tril(np.ones((SUB, SUB), bool))
+        assert np.isfinite(total[keep]).all()
+        np.testing.assert_allclose(total[keep], direct[keep], rtol=1e-4, atol=1e-6)
+
+
 def test_split_diagonal_block():
     """Unbounded gate, sub-chunk gate sums below -118 (log2 units) whose 8-token halves each
     span at most 200: the diagonal 16x16 block in its split form -- entries within a half
