@@ -133,6 +133,55 @@ bool plan_windows(int64_t B, int64_t T, int64_t H, bool final_fp32, size_t bytes
   return true;
 }
 
+// Varlen calls given less workspace than the full layout run in windows of chunk slots:
+// launch pair w is the intra kernel over slots w * nc_win .. (w + 1) * nc_win - 1 and the
+// chain over the parts of the sequences inside them (the scheduler lists, per window, the
+// sequences with chunks that reach into it). A sequence that crosses a window boundary
+// passes its state to the next window in fp32 through one of two carry slots (at most one
+// sequence crosses each boundary); sequences without chunks take their initial state (or
+// zeros) in a kernel of their own, since no window visits them. Results are bit-identical
+// to one launch pair. Layout: records | seq_tab | chunk_tab | seq_span | seq_order | nz_seq
+// | win_first | carry.
+struct VWindows {
+  int64_t count = 0, nc_win = 0;
+  size_t rec = 0, seq_tab = 0, chunk_tab = 0, seq_span = 0, seq_order = 0, nz_seq = 0, win_first = 0, carry = 0,
+         total = 0;
+};
+size_t vwindow_fixed_bytes(int64_t N, int64_t max_chunks, int64_t H) {
+  return align_up((size_t)N * sizeof(int2)) * 2 + align_up((size_t)max_chunks * sizeof(int2)) +
+         align_up((size_t)N * sizeof(int32_t)) * 2 + align_up((size_t)(max_chunks + 1) * sizeof(int32_t)) +
+         align_up((size_t)2 * H * kda::VD * kda::KD * sizeof(float));
+}
+bool plan_vwindows(int64_t T, int64_t H, int64_t N, size_t bytes, VWindows& W) {
+  const int64_t max_chunks = T / kda::CH + N;
+  if (max_chunks < 1) return false;
+  const size_t fixed = vwindow_fixed_bytes(N, max_chunks, H);
+  const size_t slot = (size_t)H * kda::REC_BYTES;   // a multiple of 256
+  if (bytes < fixed + slot) return false;
+  const int64_t fit = (int64_t)((bytes - fixed) / slot);
+  W.count = (max_chunks + fit - 1) / fit;
+  W.nc_win = (max_chunks + W.count - 1) / W.count;
+  size_t off = 0;
+  W.rec = off;
+  off += (size_t)W.nc_win * slot;
+  W.seq_tab = off;
+  off += align_up((size_t)N * sizeof(int2));
+  W.chunk_tab = off;
+  off += align_up((size_t)max_chunks * sizeof(int2));
+  W.seq_span = off;
+  off += align_up((size_t)N * sizeof(int2));
+  W.seq_order = off;
+  off += align_up((size_t)N * sizeof(int32_t));
+  W.nz_seq = off;
+  off += align_up((size_t)N * sizeof(int32_t));
+  W.win_first = off;
+  off += align_up((size_t)(max_chunks + 1) * sizeof(int32_t));
+  W.carry = off;
+  off += align_up((size_t)2 * H * kda::VD * kda::KD * sizeof(float));
+  W.total = off;
+  return W.total <= bytes;
+}
+
 // Calls that kda_fwd / kda_fwd_ex hand to the token-recurrent kernel: fixed-length rows of
 // at most REC_MAX_T tokens, or varlen batches of at most REC_MAX_AVG tokens per sequence on
 // average (the lengths themselves stay on the device). The chunked path costs a full
@@ -287,18 +336,24 @@ size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N) {
   if (!make_layout(B, T, H, N, N > 0, L)) return 0;
   // fixed-length calls on the plain chain: windows of chunk columns within WORKSPACE_TARGET
   // (at T = 32768, B = 4, H = 64 the full 9.5 GiB and 1 GiB in ten windows take the same time)
-  Windows W;
-  if (N == 0 && L.nseg == 1 && L.total > WORKSPACE_TARGET &&
-      plan_windows(B, T, H, false, WORKSPACE_TARGET, W) && W.total < L.total)
-    return W.total;
+  if (L.nseg == 1 && L.total > WORKSPACE_TARGET) {
+    if (N == 0) {
+      Windows W;
+      if (plan_windows(B, T, H, false, WORKSPACE_TARGET, W) && W.total < L.total) return W.total;
+    } else {
+      VWindows V;
+      if (plan_vwindows(T, H, N, WORKSPACE_TARGET, V) && V.total < L.total) return V.total;
+    }
+  }
   return L.total;
 }
 
 size_t kda_fwd_workspace_min(int64_t B, int64_t T, int64_t H, int64_t N) {
   Layout L;
   if (!make_layout(B, T, H, N, N > 0, L)) return 0;
-  if (N > 0 || L.total == 0) return L.total;
-  const size_t one = carry_bytes(B, H) + column_bytes(B, H);   // one chunk column and a carry
+  if (L.total == 0) return 0;
+  const size_t one = N > 0 ? vwindow_fixed_bytes(N, L.max_chunks, H) + (size_t)H * kda::REC_BYTES   // one slot
+                           : carry_bytes(B, H) + column_bytes(B, H);   // one chunk column and a carry
   return one < L.total ? one : L.total;
 }
 
@@ -322,11 +377,13 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
   const bool varlen = cu_seqlens != nullptr;
   Layout L;
   if (!make_layout(B, T, H, varlen ? N : 0, varlen, L)) return KDA_ERR_SHAPE;
-  Windows W;   // W.count > 0: the call runs in windows of chunk columns (fixed length only)
+  Windows W;    // W.count > 0: the call runs in windows of chunk columns (fixed length)
+  VWindows VW;   // VW.count > 0: in windows of chunk slots (varlen)
   if (L.total > 0) {
     if (!workspace) return KDA_ERR_WORKSPACE;
     if (workspace_bytes < L.total &&
-        (varlen || !plan_windows(B, T, H, final_dtype == KDA_STATE_FP32, workspace_bytes, W)))
+        !(varlen ? plan_vwindows(T, H, N, workspace_bytes, VW)
+                 : plan_windows(B, T, H, final_dtype == KDA_STATE_FP32, workspace_bytes, W)))
       return KDA_ERR_WORKSPACE;
     if (!aligned(workspace, ALIGN)) return KDA_ERR_ALIGN;
   }
@@ -376,6 +433,38 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
       const bool last = w + 1 == W.count;
       p.final_state = last ? final_state : carry;
       p.final_dtype = last ? final_dtype : KDA_STATE_FP32;
+      e = kda::launch_intra(p, st);
+      if (e == hipSuccess) e = kda::launch_chain(p, st);
+    }
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  }
+  if (VW.count > 0) {   // varlen windows of chunk slots (no per-kernel timing for these calls)
+    if (env_flag("KDA_LOG"))
+      std::fprintf(stderr, "[kda] fwd T=%lld H=%lld N=%lld windows=%lld x %lld slots workspace=%zu of %zu\n",
+                   (long long)T, (long long)H, (long long)N, (long long)VW.count, (long long)VW.nc_win, VW.total,
+                   L.total);
+    p.rec = ws + VW.rec;
+    p.map.seq_tab = reinterpret_cast<const int2*>(ws + VW.seq_tab);
+    p.map.chunk_tab = reinterpret_cast<const int2*>(ws + VW.chunk_tab);
+    p.map.seq_span = reinterpret_cast<const int2*>(ws + VW.seq_span);
+    p.map.seq_order = nullptr;
+    p.map.nz_seq = reinterpret_cast<const int32_t*>(ws + VW.nz_seq);
+    p.map.win_first = reinterpret_cast<const int32_t*>(ws + VW.win_first);
+    p.map.carry = reinterpret_cast<float*>(ws + VW.carry);
+    p.map.n_win = (int32_t)VW.count;
+    hipError_t e = kda::launch_sched(cu_seqlens, (int32_t)N, (int32_t)T, (int32_t)L.max_chunks,
+                                     reinterpret_cast<int2*>(ws + VW.seq_tab), reinterpret_cast<int2*>(ws + VW.chunk_tab),
+                                     reinterpret_cast<int2*>(ws + VW.seq_span), reinterpret_cast<int32_t*>(ws + VW.seq_order),
+                                     st, (int32_t)VW.nc_win, (int32_t)VW.count, reinterpret_cast<int32_t*>(ws + VW.nz_seq),
+                                     reinterpret_cast<int32_t*>(ws + VW.win_first));
+    if (e == hipSuccess) e = kda::launch_empty_states(p, (int32_t)N, st);
+    for (int64_t w = 0; w < VW.count && e == hipSuccess; ++w) {
+      const int64_t jb = w * VW.nc_win;
+      p.map.jb = (int32_t)jb;
+      p.map.nc_win = (int32_t)VW.nc_win;
+      p.map.max_chunks = (int32_t)std::min<int64_t>(VW.nc_win, L.max_chunks - jb);
+      p.map.win = (int32_t)w;
+      p.map.nseq = (int32_t)(VW.nc_win + 1);   // the chain's sequence capacity per window
       e = kda::launch_intra(p, st);
       if (e == hipSuccess) e = kda::launch_chain(p, st);
     }

@@ -135,12 +135,24 @@ __global__ __launch_bounds__((3 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
   if (nh >= NH) return;   // uniform over the block
   // varlen: walk the sequences longest first, so long chains do not start last
   const int rank = nh / H, h = nh - rank * H;
-  const int n = (mode == CHAIN_FULL && p.map.seq_order) ? __builtin_amdgcn_readfirstlane(p.map.seq_order[rank]) : rank;
+  // varlen window: the rank-th sequence with chunks from the window's first on, if it starts
+  // inside the window (uniform over the block)
+  const bool vwin = mode == CHAIN_FULL && p.map.win >= 0 && p.map.seq_tab;
+  int n;
+  if (vwin) {
+    const int k = __builtin_amdgcn_readfirstlane(p.map.win_first[p.map.win]) + rank;
+    if (k >= __builtin_amdgcn_readfirstlane(p.map.win_first[p.map.n_win])) return;
+    n = __builtin_amdgcn_readfirstlane(p.map.nz_seq[k]);
+    if (__builtin_amdgcn_readfirstlane(p.map.seq_tab[n].x) >= p.map.jb + p.map.nc_win) return;
+  } else {
+    n = (mode == CHAIN_FULL && p.map.seq_order) ? __builtin_amdgcn_readfirstlane(p.map.seq_order[rank]) : rank;
+  }
 
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, uniform
   const int l = threadIdx.x & 63, lt = l & 15, gq = l >> 4;
 
   int c0, nc, tok0, len;
+  bool win_in = false, win_out = false;   // (varlen window) state from / to the carry slots
   if (mode != CHAIN_FULL) {   // one segment of a row (fixed length) or a sequence (varlen)
     const int row = n / p.seg.nseg, sg = n - row * p.seg.nseg;
     int first, count, t0, length;
@@ -169,6 +181,15 @@ __global__ __launch_bounds__((3 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
     nc = __builtin_amdgcn_readfirstlane(e.y);
     tok0 = __builtin_amdgcn_readfirstlane(sp.x);
     len = __builtin_amdgcn_readfirstlane(sp.y);
+    if (vwin) {   // this window's chunks of the sequence, records indexed from the window's first slot
+      const int a = max(c0, p.map.jb), b = min(c0 + nc, p.map.jb + p.map.nc_win);
+      tok0 += (a - c0) * CH;
+      len -= (a - c0) * CH;
+      win_in = a > c0;        // the state comes from the previous window
+      win_out = b < c0 + nc;  // and goes on to the next
+      c0 = a - p.map.jb;
+      nc = b - a;
+    }
   } else {
     c0 = n * p.map.nc_win;   // this launch's chunks jb .. jb + nc_win - 1 of row n
     nc = p.map.nc_win;
@@ -287,6 +308,9 @@ __global__ __launch_bounds__((3 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
     const int hh = w & 1;
     f32x4 S[4];
     const size_t st_off = ((size_t)(n * H + h) * VD + 16 * vt + lt) * KD + 64 * hh;
+    // (varlen window) the carry slot of this window / the next, one sequence each
+    const size_t carry_off = ((size_t)h * VD + 16 * vt + lt) * KD + 64 * hh;
+    const size_t carry_slot = (size_t)H * VD * KD;
     // maps pass: tiles 0-7 are the value rows from a zero state (R), tiles 8-15 the rows
     // of the identity run without U~ (P); outputs pass: the scanned segment state
     const bool ptile = mode == CHAIN_MAPS && vt >= 8;
@@ -298,6 +322,10 @@ __global__ __launch_bounds__((3 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
         for (int jj = 0; jj < 4; ++jj) S[i][jj] = (ptile && 64 * hh + 16 * i + 4 * gq + jj == r) ? 1.0f : 0.0f;
     } else if (mode == CHAIN_OUTPUTS) {
       const float* src = p.seg.seg_init + st_off;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[i] = *reinterpret_cast<const f32x4*>(src + 16 * i + 4 * gq);
+    } else if (win_in) {
+      const float* src = p.map.carry + (size_t)(p.map.win & 1) * carry_slot + carry_off;
 #pragma unroll
       for (int i = 0; i < 4; ++i) S[i] = *reinterpret_cast<const f32x4*>(src + 16 * i + 4 * gq);
     } else if (p.init_dtype == 2) {
@@ -382,6 +410,10 @@ __global__ __launch_bounds__((3 * NW + 1) * 64) void kda_chain_kernel(FwdParams 
       for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4*>(dst + 16 * i + 4 * gq) = S[i];
     } else if (mode == CHAIN_OUTPUTS) {
       // the scan writes final_state
+    } else if (win_out) {
+      float* dst = p.map.carry + (size_t)((p.map.win + 1) & 1) * carry_slot + carry_off;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4*>(dst + 16 * i + 4 * gq) = S[i];
     } else if (p.final_dtype == 2) {
       float* dst = static_cast<float*>(p.final_state) + st_off;
 #pragma unroll
@@ -484,6 +516,28 @@ hipError_t launch_chain_nw(const FwdParams& p, int NH, int rows, hipStream_t str
 
 }  // namespace
 
+// Varlen calls in windows: final_state of the sequences without chunks, which no window's
+// chain visits (in one launch the chain writes them itself, with no steps): their initial
+// state, or zeros. One workgroup per (sequence, head); 256 threads copy its 128 x 128 state.
+__global__ __launch_bounds__(256) void kda_empty_states_kernel(FwdParams p, int32_t N) {
+  const int n = blockIdx.x / p.H, h = blockIdx.x - n * p.H;
+  if (n >= N || p.final_dtype == 0) return;
+  if (__builtin_amdgcn_readfirstlane(p.map.seq_tab[n].y) > 0) return;   // the windows carry it
+  const size_t base = (size_t)(n * p.H + h) * VD * KD;
+  const int tid = threadIdx.x;
+  for (int e = tid * 4; e < VD * KD; e += 256 * 4) {
+    if (p.final_dtype == 2) {
+      const f32x4 v = p.init_dtype == 2 ? *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.init_state) + base + e)
+                                        : f32x4{0, 0, 0, 0};
+      *reinterpret_cast<f32x4*>(static_cast<float*>(p.final_state) + base + e) = v;
+    } else {
+      const u32x2 v = p.init_dtype == 1 ? *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.init_state) + base + e)
+                                        : u32x2{0u, 0u};
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.final_state) + base + e) = v;
+    }
+  }
+}
+
 // Two value tiles per workgroup while the (sequence, head) chains alone leave
 // compute units idle (more, shorter workgroups); four once there are enough
 // chains, which halves how often each record's shared fragments are fetched.
@@ -500,6 +554,12 @@ hipError_t launch_chain(const FwdParams& p, hipStream_t stream) {
   }();
   return (int64_t)NH * (rows / 32) <= cus ? launch_chain_nw<2>(p, NH, rows, stream)
                                           : launch_chain_nw<4>(p, NH, rows, stream);
+}
+
+hipError_t launch_empty_states(const FwdParams& p, int32_t N, hipStream_t stream) {
+  if (N <= 0 || p.final_dtype == 0) return hipSuccess;
+  hipLaunchKernelGGL(kda_empty_states_kernel, dim3((unsigned)((int64_t)N * p.H)), dim3(256), 0, stream, p, N);
+  return hipGetLastError();
 }
 
 }  // namespace kda

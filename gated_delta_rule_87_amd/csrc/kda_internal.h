@@ -21,9 +21,19 @@ struct ChunkMap {
   const int32_t* seq_order;  // varlen: [N] sequences by chunk count, longest first
   int32_t T;               // tokens per row (fixed) / packed total (varlen)
   int32_t nc_row;          // chunks per row (fixed)
-  int32_t jb;              // first chunk of each row in this launch (fixed; 0 for varlen)
-  int32_t nc_win;          // chunks of each row in this launch (fixed; nc_row unless windowed)
-  int32_t max_chunks;      // number of chunk slots
+  int32_t jb;              // fixed: first chunk of each row in this launch; varlen: first chunk slot
+  int32_t nc_win;          // fixed: chunks of each row in this launch (nc_row unless windowed);
+                           // varlen windows: chunk slots per window
+  int32_t max_chunks;      // number of chunk slots (of this launch)
+  // varlen calls in windows of chunk slots (win >= 0): window win covers slots jb ..
+  // jb + nc_win - 1; its sequences are nz_seq[win_first[win]] onwards (kda_sched.hip),
+  // nseq is then the launch's sequence capacity nc_win + 1, and a sequence that crosses
+  // a window boundary carries its state in fp32 through carry slot (window & 1)
+  int32_t win = -1;
+  int32_t n_win = 0;
+  const int32_t* nz_seq = nullptr;
+  const int32_t* win_first = nullptr;
+  float* carry = nullptr;  // [2][H][V][K] fp32
   int32_t nseq;            // sequences (B or N)
 };
 
@@ -65,10 +75,13 @@ struct FwdParams {
 
 hipError_t launch_sched(const int64_t* cu_seqlens, int32_t N, int32_t T, int32_t max_chunks,
                         int2* seq_tab, int2* chunk_tab, int2* seq_span, int32_t* seq_order,
-                        hipStream_t stream);
+                        hipStream_t stream, int32_t win_chunks = 0, int32_t n_win = 0,
+                        int32_t* nz_seq = nullptr, int32_t* win_first = nullptr);
 hipError_t launch_intra(const FwdParams& p, hipStream_t stream);
 hipError_t launch_chain(const FwdParams& p, hipStream_t stream);
 hipError_t launch_scan(const FwdParams& p, int32_t rows, hipStream_t stream);
 hipError_t launch_recurrent(const FwdParams& p, const int64_t* cu_seqlens, hipStream_t stream);
+// varlen windows: final_state of the sequences without chunks (their initial state, or zeros)
+hipError_t launch_empty_states(const FwdParams& p, int32_t N, hipStream_t stream);
 
 }  // namespace kda

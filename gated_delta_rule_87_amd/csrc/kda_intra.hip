@@ -312,7 +312,7 @@ __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
 
   int t0, L;
   if (p.map.chunk_tab) {
-    const int2 e = p.map.chunk_tab[ci];
+    const int2 e = p.map.chunk_tab[p.map.jb + ci];   // (jb: the window's first slot)
     t0 = e.x;
     L = e.y;
   } else {

@@ -9,6 +9,13 @@
 //   seq_order[k] = the sequence with the k-th most chunks (ties: lower index
 //                  first), so the sequential state chains start longest first;
 //                  input order when N > SORT_MAX
+// and, for a call run in windows of win_chunks chunk slots (win_chunks > 0):
+//   nz_seq[k]    = the k-th sequence with at least one chunk, in index (and so in
+//                  chunk) order
+//   win_first[w] = the first k whose sequence ends after chunk slot w * win_chunks,
+//                  for w = 0 .. n_win (win_first[n_win] = the number of such sequences):
+//                  window w's sequences are nz_seq[win_first[w]] onwards, up to the
+//                  first that starts at or after its end
 // Chunks never straddle sequences; a sequence's last chunk may be partial.
 // Every sequence is clamped into [0, T] and the chunk count into the slot
 // budget floor(T/64) + N, so malformed contents cannot drive the other kernels
@@ -25,7 +32,9 @@ constexpr int SORT_MAX = 4096;   // sequences sorted in LDS (bitonic); beyond: i
 __global__ __launch_bounds__(SCHED_THREADS) void kda_sched_kernel(const int64_t* cu, int32_t N, int32_t T,
                                                                   int32_t max_chunks, int2* seq_tab,
                                                                   int2* chunk_tab, int2* seq_span,
-                                                                  int32_t* seq_order) {
+                                                                  int32_t* seq_order, int32_t win_chunks,
+                                                                  int32_t n_win, int32_t* nz_seq,
+                                                                  int32_t* win_first) {
   __shared__ int32_t warp_sums[SCHED_THREADS / 64];
   __shared__ uint64_t keys[SORT_MAX];
   __shared__ int2 s_tab[SORT_MAX], s_span[SORT_MAX];   // LDS copies of the tables (N <= SORT_MAX)
@@ -105,6 +114,44 @@ __global__ __launch_bounds__(SCHED_THREADS) void kda_sched_kernel(const int64_t*
     chunk_tab[i] = e;
   }
 
+  // windowed calls: the sequences with chunks, compacted in order, and each window's first
+  if (win_chunks > 0) {
+    if (tid == 0) carry_s = 0;
+    __syncthreads();
+    for (int base = 0; base < N; base += SCHED_THREADS) {
+      const int n = base + tid;
+      const int32_t nzf = (n < N && tab(n).y > 0) ? 1 : 0;
+      int32_t x = nzf;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int32_t y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      if (lane == 63) warp_sums[wid] = x;
+      __syncthreads();
+      int32_t woff = 0;
+      for (int k = 0; k < wid; ++k) woff += warp_sums[k];
+      const int32_t carry = carry_s;
+      if (nzf) nz_seq[carry + woff + x - 1] = n;
+      __syncthreads();
+      if (tid == SCHED_THREADS - 1) carry_s = carry + woff + x;
+      __syncthreads();
+    }
+    __threadfence_block();
+    __syncthreads();
+    const int32_t nzc = carry_s;
+    for (int w = tid; w <= n_win; w += SCHED_THREADS) {
+      const int64_t cb = (int64_t)w * win_chunks;
+      int lo = 0, hi = nzc;   // first k with end(k) > cb (ends increase with k)
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        const int2 e = tab(nz_seq[mid]);
+        if ((int64_t)e.x + e.y > cb) hi = mid; else lo = mid + 1;
+      }
+      win_first[w] = w == n_win ? nzc : lo;
+    }
+  }
+
   // pass 3: longest-first order of the sequences. Key = (INT32_MAX - chunks) << 32 | n,
   // sorted ascending by a bitonic network over the next power of two >= N.
   if (N > SORT_MAX) {
@@ -137,9 +184,10 @@ __global__ __launch_bounds__(SCHED_THREADS) void kda_sched_kernel(const int64_t*
 }  // namespace
 
 hipError_t launch_sched(const int64_t* cu_seqlens, int32_t N, int32_t T, int32_t max_chunks, int2* seq_tab,
-                        int2* chunk_tab, int2* seq_span, int32_t* seq_order, hipStream_t stream) {
+                        int2* chunk_tab, int2* seq_span, int32_t* seq_order, hipStream_t stream,
+                        int32_t win_chunks, int32_t n_win, int32_t* nz_seq, int32_t* win_first) {
   hipLaunchKernelGGL(kda_sched_kernel, dim3(1), dim3(SCHED_THREADS), 0, stream, cu_seqlens, N, T, max_chunks,
-                     seq_tab, chunk_tab, seq_span, seq_order);
+                     seq_tab, chunk_tab, seq_span, seq_order, win_chunks, n_win, nz_seq, win_first);
   return hipGetLastError();
 }
 

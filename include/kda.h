@@ -60,8 +60,7 @@ enum kda_status {
                               scale not finite, unknown flag bits, bad cu_seqlens
                               contents (KDA_VALIDATE=1 only)                        */
     KDA_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                      */
-    KDA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than kda_fwd_workspace_size
-                              (fixed length: kda_fwd_workspace_min) */
+    KDA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than kda_fwd_workspace_min */
     KDA_ERR_HIP = 7,       /* a HIP runtime call or kernel launch failed            */
     KDA_ERR_CAPACITY = 8   /* kda_fwd_noalloc: the call needs more workspace than
                               its fixed device array holds (KDA_NOALLOC_CAPACITY)   */
@@ -116,24 +115,28 @@ enum kda_state_dtype {
  * segment-parallel state chain: each row's or sequence's chunks are cut into s
  * segments (s chosen from B or N, T and H), with 192 KiB per (row or sequence,
  * segment, head) for the segments' affine maps and initial states.
- * Fixed-length calls whose full workspace would exceed 1 GiB and that use the
- * plain chain get the size of a windowed run within 1 GiB instead (windows of
- * chunk columns, see kda_fwd_workspace_min; at B = 4, T = 32768, H = 64 that
- * takes the same time as the full 9.5 GiB). Varlen calls get the full size.
+ * Calls whose full workspace would exceed 1 GiB and that use the plain chain
+ * get the size of a windowed run within 1 GiB instead (see
+ * kda_fwd_workspace_min; at B = 4, T = 32768, H = 64 that takes the same time
+ * as the full 9.5 GiB).
  */
 size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N);
 
 /*
  * kda_fwd_workspace_min -- the smallest workspace kda_fwd / kda_fwd_ex accept for
  * the same call (same arguments and invalid-size rule as kda_fwd_workspace_size).
- * Fixed-length calls (N = 0) given less than kda_fwd_workspace_size run in
- * windows of chunk columns: each window is the intra-chunk pass and the state
- * chain over chunks jb .. jb + w - 1 of every row, with each row's state
- * carried to the next window in fp32 (in final_state itself when that is fp32,
- * else in the workspace: 64 KiB per (row, head)). The minimum holds one chunk
- * column (B * H records of 74.5 KiB) and the carry. Windowed calls return the
- * same bits as unwindowed ones; they take more kernel launches and skip the
- * segment-parallel chain. Varlen calls (N > 0) need kda_fwd_workspace_size.
+ * Calls given less than kda_fwd_workspace_size run in windows, each the
+ * intra-chunk pass and the state chain over part of the chunks:
+ *   - fixed length (N = 0): chunk columns jb .. jb + w - 1 of every row, with
+ *     each row's state carried to the next window in fp32 (in final_state itself
+ *     when that is fp32, else in the workspace: 64 KiB per (row, head)); the
+ *     minimum holds one chunk column (B * H records of 74.5 KiB) and the carry;
+ *   - varlen (N > 0): w consecutive chunk slots of the packed sequences, a
+ *     sequence that crosses a window boundary carrying its state in fp32 through
+ *     one of two carry slots (64 KiB per head each); the minimum holds the
+ *     scheduler's tables, the carry slots and one slot of H records.
+ * Windowed calls return the same bits as unwindowed ones; they take more kernel
+ * launches and skip the segment-parallel chain.
  */
 size_t kda_fwd_workspace_min(int64_t B, int64_t T, int64_t H, int64_t N);
 
@@ -167,12 +170,11 @@ size_t kda_fwd_workspace_min(int64_t B, int64_t T, int64_t H, int64_t N);
  *                                    only writes final_state (the initial
  *                                    state, or zeros, for every sequence)
  *   workspace, workspace_bytes       caller-owned device scratch of at least
- *                                    kda_fwd_workspace_size(B, T, H, N) bytes
- *                                    (fixed length: at least
- *                                    kda_fwd_workspace_min, run in windows when
- *                                    below the full size), 256-byte aligned; its
- *                                    contents need no initialisation and are
- *                                    clobbered
+ *                                    kda_fwd_workspace_min(B, T, H, N) bytes
+ *                                    (run in windows when below
+ *                                    kda_fwd_workspace_size), 256-byte aligned;
+ *                                    its contents need no initialisation and
+ *                                    are clobbered
  *   stream       hipStream_t as void*
  * Returns a kda_status.
  *
@@ -231,11 +233,10 @@ int kda_fwd_recurrent_ex(const void *q, const void *k, const void *v, const void
  * of KDA_NOALLOC_CAPACITY bytes in device memory that the library holds on
  * every GPU it runs on, from its first use there until the process ends. The
  * call itself allocates nothing and issues no memset or copy.
- *   - Fixed-length calls whose full workspace exceeds the capacity run in
- *     windows of chunk columns (see kda_fwd_workspace_min); calls whose
- *     kda_fwd_workspace_min(B, T, H, N) exceeds it (varlen calls beyond
- *     3,500 chunk-heads at 74.5 KiB each, e.g. T = 4096 at H = 54; fixed-length
- *     calls with B * H beyond about 1,890) are rejected on the host with
+ *   - Calls whose full workspace exceeds the capacity run in windows (see
+ *     kda_fwd_workspace_min); calls whose kda_fwd_workspace_min(B, T, H, N)
+ *     exceeds it (fixed length: B * H beyond about 1,890; varlen: H beyond
+ *     about 1,300 at moderate T and N) are rejected on the host with
  *     KDA_ERR_CAPACITY, before anything is launched. Decode-sized calls need
  *     no workspace at all.
  *   - The array of the CURRENT device is used: `stream` must belong to it.

@@ -131,10 +131,10 @@ def test_workspace_errors():
     # fixed length: below the windowed minimum is rejected before anything is launched
     mn = kda.workspace_min(2, 1000, 4)
     assert call(B=2, T=1000, H=4, ws=FAKE, wsb=mn - 1) == EWS
-    # varlen: the full size is the minimum
-    full = kda.workspace_size(1, 1000, 4, 3)
-    assert kda.workspace_min(1, 1000, 4, 3) == full
-    assert call(T=1000, H=4, cu=FAKE, N=3, ws=FAKE, wsb=full - 1) == EWS
+    # varlen: below the windowed minimum (tables, two carry slots, one slot of records)
+    vmn = kda.workspace_min(1, 1000, 4, 3)
+    assert vmn < kda.workspace_size(1, 1000, 4, 3)
+    assert call(T=1000, H=4, cu=FAKE, N=3, ws=FAKE, wsb=vmn - 1) == EWS
 
 
 def test_workspace_min():
@@ -146,7 +146,15 @@ def test_workspace_min():
         full = kda.workspace_size(B, T, H)
         assert kda.workspace_min(B, T, H) == min(full, al(B * H * 128 * 128 * 4) + B * H * rec)
     assert kda.workspace_min(1, 64, 2) == kda.workspace_size(1, 64, 2)    # one chunk per row
-    assert kda.workspace_min(1, 8192, 64, 8) == kda.workspace_size(1, 8192, 64, 8)
+    # varlen: the tables (seq_tab, seq_span: 8 B per sequence; chunk_tab 8 B per chunk slot;
+    # seq_order, nz_seq 4 B per sequence; win_first 4 B per slot + 1), two fp32 carry slots
+    # of H states and one slot of H records
+    for T, H, N in [(8192, 64, 8), (1000, 4, 3), (131072, 64, 32)]:
+        mc = T // 64 + N
+        fixed = 2 * al(N * 8) + al(mc * 8) + 2 * al(N * 4) + al((mc + 1) * 4) + al(2 * H * 128 * 128 * 4)
+        assert kda.workspace_min(1, T, H, N) == min(kda.workspace_size(1, T, H, N), fixed + H * rec)
+    # beyond 1 GiB on the plain chain, varlen calls also get a windowed size within 1 GiB
+    assert kda.workspace_size(1, 131072, 64, 32) <= 1 << 30
     assert kda.workspace_min(1, 0, 4) == 0 and kda.workspace_min(0, 10, 4) == 0
 
 
@@ -257,15 +265,15 @@ def test_workspace_size_with_segmented_chain():
 
 def test_noalloc_capacity_check_on_host():
     """kda_fwd_noalloc rejects, before any HIP call (KDA_ERR_CAPACITY), a call whose
-    smallest workspace (kda_fwd_workspace_min) exceeds its fixed array: varlen calls
-    beyond the array, fixed-length calls whose single chunk column and carry do not fit.
+    smallest workspace (kda_fwd_workspace_min) exceeds its fixed array: calls whose
+    single window (one chunk column or slot of records, and the carry) does not fit.
     The capacity is the header's 256 MiB."""
     L = kda.lib()
     cap = L.kda_noalloc_capacity()
     assert cap == 256 << 20
-    assert kda.workspace_size(1, 8192, 64, 4) > cap >= kda.workspace_size(1, 4096, 54, 1)
+    assert kda.workspace_min(1, 64, 2048, 1) > cap >= kda.workspace_min(1, 8192, 64, 4)
     assert kda.workspace_min(16, 8192, 128) > cap >= kda.workspace_min(1, 8192, 64)
     P = ctypes.c_void_p
     args = [P(FAKE)] * 5 + [0.088, P(FAKE), P(FAKE), P(FAKE), -5.0, None, 0, None, 0]
-    assert L.kda_fwd_noalloc(*args, P(FAKE), 4, 1, 8192, 64, 128, 128, 7, None) == ECAP    # varlen
+    assert L.kda_fwd_noalloc(*args, P(FAKE), 1, 1, 64, 2048, 128, 128, 7, None) == ECAP    # varlen, H too large
     assert L.kda_fwd_noalloc(*args, None, 0, 16, 8192, 128, 128, 128, 7, None) == ECAP    # B * H too large

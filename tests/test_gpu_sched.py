@@ -100,3 +100,50 @@ def test_schedule_order_beyond_sort_limit():
     assert np.array_equal(seq_tab, e_tab) and np.array_equal(seq_span, e_span)
     assert np.array_equal(chunk_tab, e_chunk)
     assert np.array_equal(seq_order, np.arange(len(lengths)))
+
+
+@pytest.mark.parametrize("lengths,width", [
+    ([0, 1, 15, 16, 17, 63, 64, 65, 127, 129], 1),
+    ([300, 0, 5, 300, 64, 0], 2),
+    ([0, 0, 2000, 0, 7], 4),
+    (list(np.random.default_rng(4).integers(0, 500, 41)), 3),
+])
+def test_window_tables(lengths, width):
+    """A varlen call in windows of `width` chunk slots: the scheduler's window tables, read
+    back from the windowed workspace (records | seq_tab | chunk_tab | seq_span | seq_order |
+    nz_seq | win_first | carry), against the same lists built in Python:
+      nz_seq[k]    = the k-th sequence with at least one chunk, in index order
+      win_first[w] = the first k whose sequence ends after slot w * width (w = 0 .. windows),
+                     and the number of such sequences for w = windows."""
+    device = torch.device("cuda:0")
+    H = 1
+    w = kda_inputs.custom(lengths=list(lengths), H=H, final=None)
+    d = kda_inputs.make_inputs(w)
+    x = {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    T, N = w.T, len(lengths)
+    mc = T // 64 + N
+    fixed = 2 * al(N * 8) + al(mc * 8) + 2 * al(N * 4) + al((mc + 1) * 4) + al(2 * H * 128 * 128 * 4)
+    ws_bytes = fixed + width * H * REC
+    assert ws_bytes < kda.workspace_size(1, T, H, N)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=device)
+    out = torch.empty(1, T, H, 128, dtype=torch.bfloat16, device=device)
+    kda.fwd(x['q'], x['k'], x['v'], x['g'], x['beta'], x['scale'], out, x['A_log'], x['dt_bias'],
+            x['lower_bound'], cu_seqlens=x['cu_seqlens'], workspace=ws, force_chunked=True)
+    torch.cuda.synchronize()
+    b = ws.cpu().numpy()
+    count = -(-mc // width)                  # fewest windows that fit, then balanced widths
+    wd = -(-mc // count)
+    assert wd == width
+    off = wd * H * REC
+    seq_tab = b[off:off + 8 * N].view(np.int32).reshape(N, 2)
+    off = al(off + 8 * N) + al(8 * mc) + al(8 * N) + al(4 * N)
+    nz_seq = b[off:off + 4 * N].view(np.int32)
+    off = al(off + 4 * N)
+    win_first = b[off:off + 4 * (count + 1)].view(np.int32)
+    _, ref_tab, _, _, _ = expected_tables(lengths, T)
+    assert np.array_equal(seq_tab, ref_tab)
+    nz = [n for n in range(N) if ref_tab[n, 1] > 0]
+    assert np.array_equal(nz_seq[:len(nz)], nz)
+    ends = [ref_tab[n, 0] + ref_tab[n, 1] for n in nz]
+    ref_first = [next((k for k, e in enumerate(ends) if e > wi * wd), len(nz)) for wi in range(count)] + [len(nz)]
+    assert np.array_equal(win_first, ref_first)

@@ -150,3 +150,99 @@ def test_windowed_instead_of_segmented_chain():
         frel = np.linalg.norm(f.cpu().numpy() - rf) / np.linalg.norm(rf)
         say(f"{tag}: out max-abs {np.abs(on - ro).max():.3e} rel-L2 {rel:.3e}, final rel-L2 {frel:.3e}")
         assert np.abs(on - ro).max() <= 2e-2 and rel <= 5e-3 and frel <= 2e-3
+
+
+# ---- varlen calls in windows of chunk slots --------------------------------------------
+
+def al(x):
+    return -(-x // 256) * 256
+
+
+def vws_for_width(T, H, N, width):
+    """Workspace bytes that give varlen windows of `width` chunk slots (tables, two carry
+    slots of fp32 state and `width` slots of records; see plan_vwindows)."""
+    mc = T // CH + N
+    fixed = 2 * al(N * 8) + al(mc * 8) + 2 * al(N * 4) + al((mc + 1) * 4) + al(2 * H * 128 * 128 * 4)
+    return fixed + width * H * kda.record_bytes()
+
+
+def vinputs(lengths, H, seed, state, lower_bound=-5.0):
+    w = kda_inputs.custom(lengths=lengths, H=H, state=state, final=state or 'fp32', seed=seed,
+                          lower_bound=lower_bound)
+    d = kda_inputs.make_inputs(w)
+    return w, {k: (v.to(dev()) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+
+
+def vrun(w, x, ws_bytes, fin_dtype, init=None, alias=False, safe_gate=True):
+    T, H, N = w.T, w.H, w.n_seqs
+    out = torch.full((1, T, H, 128), float('nan'), dtype=torch.bfloat16, device=dev())
+    fin = init if alias else (None if fin_dtype is None else
+                              torch.full((N, H, 128, 128), float('nan'), dtype=fin_dtype, device=dev()))
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev())
+    kda.fwd(x['q'], x['k'], x['v'], x['g'], x['beta'], x['scale'], out, x['A_log'], x['dt_bias'],
+            x['lower_bound'], initial_state=init, final_state=fin, cu_seqlens=x['cu_seqlens'], workspace=ws,
+            safe_gate=safe_gate)
+    torch.cuda.synchronize()
+    return out, fin
+
+
+def same_bits(a, b):
+    if a.dtype == torch.bfloat16:
+        return torch.equal(a.view(torch.int16), b.view(torch.int16))
+    return torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+# lengths: empty sequences, one token, exact chunk multiples, long ones crossing many windows
+VLENGTHS = [
+    [700, 0, 3, 1500, 64, 0, 129, 1],
+    [0, 0, 2000],
+    [64] * 12 + [1000],
+    [5, 0, 0, 7, 300, 0],
+]
+
+
+@pytest.mark.parametrize("lengths", VLENGTHS)
+@pytest.mark.parametrize("states", [(None, torch.float32, False), (torch.float32, torch.float32, False),
+                                    (torch.bfloat16, torch.bfloat16, False), (torch.float32, torch.float32, True),
+                                    (torch.bfloat16, None, False)])
+def test_varlen_windowed_bit_identical(lengths, states):
+    idt, fdt, alias = states
+    H = 3
+    sname = {None: None, torch.float32: 'fp32', torch.bfloat16: 'bf16'}[idt]
+    w, x = vinputs(lengths, H, seed=len(lengths) * 7 + sum(lengths) % 97, state=sname)
+    T, N = w.T, w.n_seqs
+    init = x['initial_state']
+    full = kda.workspace_size(1, T, H, N)
+    o_ref, f_ref = vrun(w, x, full, fdt, init=init.clone() if alias else init, alias=alias)
+    mc = T // CH + N
+    for width in sorted({1, 2, 5, max(1, mc // 2)}):
+        if width >= mc:
+            continue
+        wsb = vws_for_width(T, H, N, width)
+        assert kda.workspace_min(1, T, H, N) <= wsb < full
+        o, f = vrun(w, x, wsb, fdt, init=init.clone() if alias else init, alias=alias)
+        say(f"lengths={lengths} states={states} width={width}: windows={-(-mc // width)}")
+        assert same_bits(o, o_ref), f"out differs at width {width}"
+        if f_ref is not None:
+            assert same_bits(f, f_ref), f"final_state differs at width {width}"
+
+
+def test_varlen_windowed_unbounded_gate_and_oracle():
+    lengths = [300, 0, 900, 17]
+    w, x = vinputs(lengths, 2, seed=5, state='fp32')
+    T, H, N = w.T, w.H, w.n_seqs
+    for safe in (True, False):
+        o_ref, f_ref = vrun(w, x, kda.workspace_size(1, T, H, N), torch.float32, init=x['initial_state'],
+                            safe_gate=safe)
+        o, f = vrun(w, x, vws_for_width(T, H, N, 3), torch.float32, init=x['initial_state'], safe_gate=safe)
+        assert same_bits(o, o_ref) and same_bits(f, f_ref), f"safe_gate={safe}"
+    c = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    ro, rf = kda_oracle(c['q'], c['k'], c['v'], c['g'], c['beta'], c['scale'], c['A_log'], c['dt_bias'],
+                        c['lower_bound'], initial_state=c['initial_state'], cu_seqlens=c['cu_seqlens'],
+                        safe_gate=False)
+    on = o.float().cpu().numpy().astype(np.float64).reshape(np.asarray(ro).shape)
+    rel = np.linalg.norm(on - ro) / np.linalg.norm(ro)
+    frel = np.linalg.norm(f.cpu().numpy() - rf) / np.linalg.norm(rf)
+    say(f"varlen windowed (unbounded) vs oracle: out max-abs {np.abs(on - ro).max():.3e} rel-L2 {rel:.3e}, "
+        f"final rel-L2 {frel:.3e}")
+    assert np.abs(on - ro).max() <= 2e-2 and rel <= 5e-3 and frel <= 2e-3

@@ -117,19 +117,37 @@ def test_noalloc_windowed_beyond_capacity():
             "final differs"
 
 
-def test_noalloc_rejects_beyond_capacity():
-    """Two varlen sequences of 4096 tokens at H = 64 need 635 MB of workspace, and varlen
-    calls do not run in windows: rejected on the host, nothing written."""
+def test_noalloc_varlen_windowed_beyond_capacity():
+    """Two varlen sequences of 4096 tokens at H = 64 need 635 MB of workspace for one launch
+    pair: the no-alloc entry runs them in windows of chunk slots, bit-identical to kda_fwd_ex
+    with the full workspace."""
     device = torch.device("cuda:0")
-    w = kda_inputs.custom(lengths=[4096, 4096], H=64)
-    assert kda.workspace_min(1, 8192, 64, 2) > CAPACITY
-    z = torch.zeros(1, 8192, 64, 128, dtype=torch.bfloat16, device=device)
-    x = dict(q=z, k=z, v=z, g=z, beta=torch.zeros(1, 8192, 64, dtype=torch.bfloat16, device=device),
-             A_log=torch.zeros(64, device=device), dt_bias=torch.zeros(64, 128, device=device), scale=0.1,
+    w = kda_inputs.custom(lengths=[4096, 0, 4096, 5], H=64, state='bf16', final='bf16')
+    assert kda.workspace_size(1, w.T, 64, 4) > CAPACITY >= kda.workspace_min(1, w.T, 64, 4)
+    d = kda_inputs.make_inputs(w)
+    x = {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    o1, f1 = _run("noalloc", w, x)
+    o2, f2 = _run("ex", w, x)
+    assert torch.isfinite(o1.float()).all() and torch.isfinite(f1.float()).all()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), "out differs"
+    assert torch.equal(f1.view(torch.int16), f2.view(torch.int16)), "final differs"
+
+
+def test_noalloc_rejects_beyond_capacity():
+    """One varlen sequence of 64 tokens at H = 2048: a single window (one slot of 2048
+    records and two carry slots of 2048 fp32 states) exceeds the 256 MiB array, so the call
+    is rejected on the host and nothing is written."""
+    device = torch.device("cuda:0")
+    H = 2048
+    w = kda_inputs.custom(lengths=[64], H=H)
+    assert kda.workspace_min(1, 64, H, 1) > CAPACITY
+    z = torch.zeros(1, 64, H, 128, dtype=torch.bfloat16, device=device)
+    x = dict(q=z, k=z, v=z, g=z, beta=torch.zeros(1, 64, H, dtype=torch.bfloat16, device=device),
+             A_log=torch.zeros(H, device=device), dt_bias=torch.zeros(H, 128, device=device), scale=0.1,
              lower_bound=-5.0, initial_state=None,
-             cu_seqlens=torch.tensor([0, 4096, 8192], dtype=torch.int64, device=device))
+             cu_seqlens=torch.tensor([0, 64], dtype=torch.int64, device=device))
     out = torch.full_like(z, float('nan'))
-    fin = torch.full((2, 64, 128, 128), float('nan'), device=device)
+    fin = torch.full((1, H, 128, 128), float('nan'), device=device)
     rc = _call("noalloc", w, x, out, fin)
     assert rc == KDA_ERR_CAPACITY, kda.status_string(rc)
     torch.cuda.synchronize()
