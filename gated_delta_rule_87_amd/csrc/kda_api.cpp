@@ -334,8 +334,8 @@ extern "C" {
 size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t N) {
   Layout L;
   if (!make_layout(B, T, H, N, N > 0, L)) return 0;
-  // fixed-length calls on the plain chain: windows of chunk columns within WORKSPACE_TARGET
-  // (at T = 32768, B = 4, H = 64 the full 9.5 GiB and 1 GiB in ten windows take the same time)
+  // calls on the plain chain: windows within WORKSPACE_TARGET (at T = 32768, B = 4, H = 64
+  // the full 9.5 GiB and 1 GiB in ten windows take the same time)
   if (L.nseg == 1 && L.total > WORKSPACE_TARGET) {
     if (N == 0) {
       Windows W;
@@ -464,7 +464,9 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
       p.map.nc_win = (int32_t)VW.nc_win;
       p.map.max_chunks = (int32_t)std::min<int64_t>(VW.nc_win, L.max_chunks - jb);
       p.map.win = (int32_t)w;
-      p.map.nseq = (int32_t)(VW.nc_win + 1);   // the chain's sequence capacity per window
+      // the chain's sequence capacity per window: a window meets at most nc_win + 1
+      // sequences with chunks, and there are N in all
+      p.map.nseq = (int32_t)std::min<int64_t>(VW.nc_win + 1, N);
       e = kda::launch_intra(p, st);
       if (e == hipSuccess) e = kda::launch_chain(p, st);
     }

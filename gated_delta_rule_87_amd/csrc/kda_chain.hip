@@ -518,22 +518,25 @@ hipError_t launch_chain_nw(const FwdParams& p, int NH, int rows, hipStream_t str
 
 // Varlen calls in windows: final_state of the sequences without chunks, which no window's
 // chain visits (in one launch the chain writes them itself, with no steps): their initial
-// state, or zeros. One workgroup per (sequence, head); 256 threads copy its 128 x 128 state.
+// state, or zeros. One workgroup per sequence (most leave at once); 256 threads copy the
+// 128 x 128 state of each head.
 __global__ __launch_bounds__(256) void kda_empty_states_kernel(FwdParams p, int32_t N) {
-  const int n = blockIdx.x / p.H, h = blockIdx.x - n * p.H;
+  const int n = blockIdx.x;
   if (n >= N || p.final_dtype == 0) return;
   if (__builtin_amdgcn_readfirstlane(p.map.seq_tab[n].y) > 0) return;   // the windows carry it
-  const size_t base = (size_t)(n * p.H + h) * VD * KD;
   const int tid = threadIdx.x;
-  for (int e = tid * 4; e < VD * KD; e += 256 * 4) {
-    if (p.final_dtype == 2) {
-      const f32x4 v = p.init_dtype == 2 ? *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.init_state) + base + e)
-                                        : f32x4{0, 0, 0, 0};
-      *reinterpret_cast<f32x4*>(static_cast<float*>(p.final_state) + base + e) = v;
-    } else {
-      const u32x2 v = p.init_dtype == 1 ? *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.init_state) + base + e)
-                                        : u32x2{0u, 0u};
-      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.final_state) + base + e) = v;
+  for (int h = 0; h < p.H; ++h) {
+    const size_t base = (size_t)(n * p.H + h) * VD * KD;
+    for (int e = tid * 4; e < VD * KD; e += 256 * 4) {
+      if (p.final_dtype == 2) {
+        const f32x4 v = p.init_dtype == 2 ? *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.init_state) + base + e)
+                                          : f32x4{0, 0, 0, 0};
+        *reinterpret_cast<f32x4*>(static_cast<float*>(p.final_state) + base + e) = v;
+      } else {
+        const u32x2 v = p.init_dtype == 1 ? *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.init_state) + base + e)
+                                          : u32x2{0u, 0u};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.final_state) + base + e) = v;
+      }
     }
   }
 }
@@ -558,7 +561,7 @@ hipError_t launch_chain(const FwdParams& p, hipStream_t stream) {
 
 hipError_t launch_empty_states(const FwdParams& p, int32_t N, hipStream_t stream) {
   if (N <= 0 || p.final_dtype == 0) return hipSuccess;
-  hipLaunchKernelGGL(kda_empty_states_kernel, dim3((unsigned)((int64_t)N * p.H)), dim3(256), 0, stream, p, N);
+  hipLaunchKernelGGL(kda_empty_states_kernel, dim3((unsigned)N), dim3(256), 0, stream, p, N);
   return hipGetLastError();
 }
 
