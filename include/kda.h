@@ -115,8 +115,8 @@ enum kda_state_dtype {
  * segment-parallel state chain: each row's or sequence's chunks are cut into s
  * segments (s chosen from B or N, T and H), with 192 KiB per (row or sequence,
  * segment, head) for the segments' affine maps and initial states.
- * Calls whose full workspace would exceed 1 GiB and that use the plain chain
- * get the size of a windowed run within 1 GiB instead (see
+ * Calls whose full workspace would exceed 4 GiB and that use the plain chain
+ * get the size of a windowed run within 4 GiB instead (see
  * kda_fwd_workspace_min; at B = 4, T = 32768, H = 64 that takes the same time
  * as the full 9.5 GiB).
  */

@@ -51,12 +51,12 @@ def test_workspace_size():
     rec = 76288                         # bytes per (64-token chunk, head)
     al = lambda x: (x + 255) // 256 * 256
     assert kda.workspace_size(1, 8192, 64) == al(128 * 64 * rec)
-    # beyond 1 GiB on the plain chain: windows of chunk columns within 1 GiB (fp32 carry of
+    # beyond 4 GiB on the plain chain: windows of chunk columns within 4 GiB (fp32 carry of
     # 64 KiB per (row, head), then the fewest windows that fit, with balanced widths)
     carry, col = al(4 * 64 * 128 * 128 * 4), 4 * 64 * rec
-    fit = ((1 << 30) - carry) // col
+    fit = ((4 << 30) - carry) // col
     count = -(-512 // fit)
-    assert kda.workspace_size(4, 32768, 64) == carry + -(-512 // count) * col <= 1 << 30
+    assert kda.workspace_size(4, 32768, 64) == carry + -(-512 // count) * col <= 4 << 30
     assert kda.workspace_size(1, 100, 2) == al(2 * 2 * rec)             # ceil(100/64) = 2
     # varlen: floor(T/64) + N chunk slots, plus the tables
     ws = kda.workspace_size(1, 8192, 64, 8)
@@ -153,8 +153,9 @@ def test_workspace_min():
         mc = T // 64 + N
         fixed = 2 * al(N * 8) + al(mc * 8) + 2 * al(N * 4) + al((mc + 1) * 4) + al(2 * H * 128 * 128 * 4)
         assert kda.workspace_min(1, T, H, N) == min(kda.workspace_size(1, T, H, N), fixed + H * rec)
-    # beyond 1 GiB on the plain chain, varlen calls also get a windowed size within 1 GiB
-    assert kda.workspace_size(1, 131072, 64, 32) <= 1 << 30
+    # beyond 4 GiB on the plain chain, varlen calls also get a windowed size within 4 GiB
+    assert kda.workspace_size(1, 131072, 64, 32) <= 4 << 30
+    assert kda.workspace_size(1, 26810, 64, 32) > 1 << 30     # 2.2 GB: one launch pair
     assert kda.workspace_min(1, 0, 4) == 0 and kda.workspace_min(0, 10, 4) == 0
 
 
