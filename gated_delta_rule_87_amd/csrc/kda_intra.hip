@@ -230,7 +230,10 @@ __device__ __forceinline__ f32x4 reduce_scatter16(const float* P) {
 // Gs (log2 units).
 // MASK: leave out the channels split_excluded() names (their factors may overflow; the
 // caller adds them entry by entry).
-template <bool MASK>
+// WHOLE: a sub-chunk whose gate sums all stay within DIAG_RANGE2_MID: every token takes the
+// midpoint g15 / 2 of its channel, so each factor is within 2^(+-100) and one product holds
+// every kept entry (no cross product, no merge).
+template <bool MASK, bool WHOLE = false>
 __device__ __forceinline__ void split_diag(const u32x4* qraw, const u32x4* kraw, const float* Gs, float rq, float rk,
                                            int lt, int gq, f32x4& aD, f32x4& qD) {
   const bool hi = lt >= 8;
@@ -249,16 +252,16 @@ __device__ __forceinline__ void split_diag(const u32x4* qraw, const u32x4* kraw,
         const int e = 2 * e2i + u;
         const float G = Gs[8 * s + e];
         const float g7 = row_bcast<7>(G), g15 = row_bcast<15>(G);   // broadcasts first, selects after
-        const float m = hi ? 0.5f * (g7 + g15) : 0.5f * g7;
+        const float m = WHOLE ? 0.5f * g15 : (hi ? 0.5f * (g7 + g15) : 0.5f * g7);
         const float up = fast_exp2(G - m), dn = fast_exp2(m - G);
-        const float ex = fast_exp2(hi ? G - g7 : g7 - G);           // <= 1
+        const float ex = WHOLE ? 0.0f : fast_exp2(hi ? G - g7 : g7 - G);   // <= 1
         const float kn = kf[e] * rk, qn = qf[e] * rq;
         v[u][0] = kn * up;
         v[u][1] = qn * up;
         v[u][2] = kn * dn;
-        v[u][3] = hi ? kn * ex : 0.0f;
-        v[u][4] = hi ? qn * ex : 0.0f;
-        v[u][5] = hi ? 0.0f : kn * ex;
+        v[u][3] = (!WHOLE && hi) ? kn * ex : 0.0f;
+        v[u][4] = (!WHOLE && hi) ? qn * ex : 0.0f;
+        v[u][5] = (WHOLE || hi) ? 0.0f : kn * ex;
         if constexpr (MASK) {
           const bool out = split_excluded(g7, g15);
 #pragma unroll
@@ -275,9 +278,12 @@ __device__ __forceinline__ void split_diag(const u32x4* qraw, const u32x4* kraw,
     const u32x4 C1 = {c1[0], c1[1], c1[2], c1[3]}, C2 = {c2[0], c2[1], c2[2], c2[3]};
     aD = mfma_bf16(u32x4{a1[0], a1[1], a1[2], a1[3]}, C1, aD);
     qD = mfma_bf16(C1, u32x4{q1[0], q1[1], q1[2], q1[3]}, qD);
-    aX = mfma_bf16(u32x4{a2[0], a2[1], a2[2], a2[3]}, C2, aX);
-    qX = mfma_bf16(C2, u32x4{q2[0], q2[1], q2[2], q2[3]}, qX);
+    if constexpr (!WHOLE) {
+      aX = mfma_bf16(u32x4{a2[0], a2[1], a2[2], a2[3]}, C2, aX);
+      qX = mfma_bf16(C2, u32x4{q2[0], q2[1], q2[2], q2[3]}, qX);
+    }
   }
+  if constexpr (WHOLE) return;
   // aD[j] = D[4gq + j][lt] (row, column); qD[j] = D[key 4gq + j][query lt]
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -296,10 +302,12 @@ constexpr float DIAG_RANGE2 = 118.0f;
 //             16-token sub-chunk spans at most 80 natural-log units and every diagonal
 //             block is formed from the factorised operands on MFMA.
 // UB = true : the gate without the safe bound. Sub-chunks whose gate sums stay within
-//             DIAG_RANGE2 take the same MFMA path; those whose 8-token halves each stay
-//             within DIAG_RANGE2_MID take the split form (split_diag); in the others the
-//             split form takes the channels within that range and pair_step1 the rest,
-//             entry by entry (wave-uniform choices, per sub-chunk and channel slot).
+//             DIAG_RANGE2 take the same MFMA path; those within DIAG_RANGE2_MID take the
+//             split form about one midpoint per channel (split_diag<false, true>); those
+//             whose 8-token halves each stay within DIAG_RANGE2_MID take the split form
+//             (split_diag); in the others the split form takes the channels within that
+//             range and pair_step1 the rest, entry by entry (wave-uniform choices, per
+//             sub-chunk and channel slot).
 template <bool UB>
 __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
   __shared__ IntraSmem sm;
@@ -339,6 +347,7 @@ __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
   float rq, rk;
   bool slow = false;   // (UB only) this sub-chunk's diagonal block is formed entry by entry
   bool split = false;  // (UB only) ... on MFMA, in the split form (split_diag)
+  bool whole = false;  // (UB only) ... about one midpoint per channel (with split set)
   // diagonal gram block of this sub-chunk: D[r][i] = k^_r.k^_i exp(Gs_r - Gs_i) and
   // D[i][r] = k^_i.q^_r exp(Gs_r - Gs_i) in D layout (MFMA path, phase B); on the
   // entry-by-entry path (phase A) aD holds the first transposed, see phase D
@@ -407,7 +416,11 @@ __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
       for (int i = 1; i < 32; ++i) mn = fminf(mn, Gs[i]);
       const float wmn = wave_min(mn);
       slow = __builtin_amdgcn_readfirstlane(wmn < -DIAG_RANGE2 ? 1 : 0) != 0;
-      if (slow) {   // the split form applies when each 8-token half spans at most DIAG_RANGE2_MID
+      whole = slow && __builtin_amdgcn_readfirstlane(wmn >= -DIAG_RANGE2_MID ? 1 : 0) != 0;
+      if (whole) {
+        split = true;
+        slow = false;
+      } else if (slow) {   // the split form applies when each 8-token half spans at most DIAG_RANGE2_MID
         // largest gate span of an 8-token half: the lanes at each half's end take the sum 8
         // lanes back (0 past the row start) minus their own
         float d2 = 0.0f;
@@ -494,7 +507,8 @@ __global__ __launch_bounds__(256, 3) void kda_intra_kernel(FwdParams p) {
 
   // ---------------- phase B: operands, diagonal grams, permuted copies -------
   f32x4 aS = {0, 0, 0, 0};   // (UB, slow sub-chunk) gram block over the channels of the split form
-  if (UB && split) split_diag<false>(qraw, kraw, Gs, rq, rk, lt, gq, aD, qD);
+  if (UB && whole) split_diag<false, true>(qraw, kraw, Gs, rq, rk, lt, gq, aD, qD);
+  else if (UB && split) split_diag<false>(qraw, kraw, Gs, rq, rk, lt, gq, aD, qD);
   if (UB && slow) {
     f32x4 qS = {0, 0, 0, 0};
     split_diag<true>(qraw, kraw, Gs, rq, rk, lt, gq, aS, qS);

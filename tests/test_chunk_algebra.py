@@ -145,6 +145,34 @@ def test_split_diagonal_block_with_excluded_channels():
         np.testing.assert_allclose(total[keep], direct[keep], rtol=1e-4, atol=1e-6)
 
 
+def test_midpoint_diagonal_block():
+    """Unbounded gate, sub-chunk gate sums in [-200, -118) (log2 units): the diagonal 16x16
+    block from factors 2^(Gs - m) (rows) and 2^(m - Gs) (columns) about one midpoint per
+    channel, m = g15 / 2 (g15: the channel's sum at token 15, its smallest), keeps every
+    factor within 2^(+-100) and, computed in fp32, gives every kept entry (key i <= row r)
+    finite and equal to the direct sum sum_c k_r k_i 2^(Gs_r - Gs_i); entries above the
+    diagonal may overflow and are masked by the kernels."""
+    rng = np.random.default_rng(7)
+    SUB, K = 16, 128
+    for total in (-119.0, -150.0, -199.9):
+        raw = rng.exponential(1.0, size=(SUB, K))
+        gates = -raw / raw.sum(0, keepdims=True).max() * (-total)
+        Gs = np.cumsum(gates, axis=0)
+        g15 = Gs[15]
+        assert -Gs.min() > 118 and -g15.min() <= 200 and np.isclose(Gs.min(), g15.min())
+        m = 0.5 * g15
+        up, dn = np.exp2(Gs - m), np.exp2(m - Gs)
+        assert np.abs(np.log2(up)).max() <= 100 and np.abs(np.log2(dn)).max() <= 100
+        k = rng.standard_normal((SUB, K))
+        k /= np.sqrt((k ** 2).sum(1, keepdims=True))
+        direct = np.einsum('rc,ic,ric->ri', k, k, np.exp2(np.minimum(Gs[:, None, :] - Gs[None, :, :], 0.0)))
+        with np.errstate(over='ignore', invalid='ignore'):
+            d = (k * up).astype(np.float32) @ (k * dn).astype(np.float32).T
+        keep = np.tril(np.ones((SUB, SUB), bool))
+        assert np.isfinite(d[keep]).all()
+        np.testing.assert_allclose(d[keep], direct[keep], rtol=1e-4, atol=1e-6)
+
+
 def test_split_diagonal_block():
     """Unbounded gate, sub-chunk gate sums below -118 (log2 units) whose 8-token halves each
     span at most 200: the diagonal 16x16 block in its split form -- entries within a half
