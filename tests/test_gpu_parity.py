@@ -349,6 +349,27 @@ def test_full_size_all_heads(idx):
     compare_all_heads(out, fin, d, w.final, w.name)
 
 
+# mid-size shapes between the small cases and the full workloads: head counts that are
+# not multiples of 8, chains on two and four value tiles per workgroup, ragged rows and
+# sequences, the segmented chain at 16 heads, every state dtype
+MEDIUM = [
+    dict(B=3, T=777, H=5, state='fp32', lower_bound=-3.0, seed=11),
+    dict(B=1, T=4099, H=12, state='bf16', final='bf16', seed=12),
+    dict(B=2, T=2048, H=24, lower_bound=-0.5, seed=13),
+    dict(lengths=[1000, 17, 2500, 64, 0, 333], H=20, state='fp32', seed=14),   # 4 value tiles per workgroup
+    dict(B=1, T=8192, H=16, seed=15),                                          # segmented chain (4 segments)
+]
+
+
+@pytest.mark.parametrize("case", range(len(MEDIUM)))
+def test_medium_shapes_all_heads(case):
+    w = kda_inputs.custom(**MEDIUM[case])
+    say(f"medium case {case} {MEDIUM[case]}: all heads")
+    d = kda_inputs.make_inputs(w)
+    out, fin = run_dev(d, w)
+    compare_all_heads(out, fin, d, w.final, f"medium {case} {w.name}")
+
+
 @pytest.mark.parametrize("path", ["recurrent", "chunked"])
 def test_decode_step_all_heads(path):
     """One generation step (one token per sequence, fp32 state in and out), every head."""
