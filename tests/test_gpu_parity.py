@@ -358,6 +358,8 @@ MEDIUM = [
     dict(B=2, T=2048, H=24, lower_bound=-0.5, seed=13),
     dict(lengths=[1000, 17, 2500, 64, 0, 333], H=20, state='fp32', seed=14),   # 4 value tiles per workgroup
     dict(B=1, T=8192, H=16, seed=15),                                          # segmented chain (4 segments)
+    dict(B=1, T=1100, H=96, seed=16),                                          # more heads than the workloads
+    dict(lengths=[700, 300, 1], H=128, state='bf16', final='bf16', seed=17),
 ]
 
 
